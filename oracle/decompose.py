@@ -1,0 +1,133 @@
+"""The analytic one-shot decomposition of per-layer weights into theta bundles.
+
+Pages: "Quality" page ("Verdict", "Why sharing fails: reconstruction error")
+and "Add a new model architecture" page ("Add the weightless fields",
+"Decompose HF weights", "Validate > Analytic").  The pages name the pieces --
+G bands of layers share one W0 (the band mean), a per-row scale s that is
+"near 1" at passthrough, a rank-r delta U V^T that absorbs the residual
+W - s W0, and the relative Frobenius error averaged over layers and families --
+but print no formula for s, the band assignment or the singular-value split.
+The readings taken here:
+
+  * G counts bands (G = L gives one layer per band, "passthrough"); layer l
+    sits in band floor(l * G / L) (contiguous, balanced bands; "5 bands (12
+    layers per band)" for 60 layers).
+  * s is the per-row least-squares scale of W against W0:
+        s_i = <W[i,:], W0[i,:]> / <W0[i,:], W0[i,:]>,  s_i = 1 if W0[i,:] = 0.
+    At passthrough this is a/a = 1 exactly.
+  * The delta is the rank-r' truncated SVD of R = W - diag(s) W0 with
+    r' = min(r, N, K), split symmetrically: U = P sqrt(S), V = Q sqrt(S).
+  * Stored dtypes follow the model dtype: W0, U, V bfloat16, s float32.  With
+    ``store=True`` W0 is rounded before s is fitted (s and the delta then fit
+    the block the forward will actually use) and U, V are rounded last.
+  * The reported error is the unweighted mean of per-matrix errors
+        e = ||W - (diag(s) W0 + U V^T)||_F / ||W||_F.
+"""
+import numpy as np
+
+from .bf16 import round_bf16
+
+
+def band_of(layer, num_layers, num_bands):
+    return (layer * num_bands) // num_layers
+
+
+def band_members(band, num_layers, num_bands):
+    return [l for l in range(num_layers) if band_of(l, num_layers, num_bands) == band]
+
+
+def shared_block(weights):
+    """Band mean of the member layers' weights."""
+    acc = np.zeros_like(np.asarray(weights[0], np.float64))
+    for W in weights:
+        acc += np.asarray(W, np.float64)
+    return acc / len(weights)
+
+
+def row_scale(W, W0):
+    """Per-row least-squares scale of W against W0."""
+    W = np.asarray(W, np.float64)
+    W0 = np.asarray(W0, np.float64)
+    num = np.einsum("ij,ij->i", W, W0)
+    den = np.einsum("ij,ij->i", W0, W0)
+    safe = np.where(den == 0.0, 1.0, den)
+    return np.where(den == 0.0, 1.0, num / safe)
+
+
+def residual(W, W0, s):
+    return np.asarray(W, np.float64) - np.asarray(s, np.float64)[:, None] * np.asarray(W0, np.float64)
+
+
+def truncated_factors(R, rank):
+    """U [N, r'], V [K, r'] with U V^T the best rank-r' approximation of R,
+    singular values split as sqrt on both sides; also returns all singular
+    values."""
+    N, K = R.shape
+    r = min(rank, N, K)
+    P, S, Qt = np.linalg.svd(R, full_matrices=False)
+    root = np.sqrt(S[:r])
+    U = P[:, :r] * root[None, :]
+    V = Qt[:r, :].T * root[None, :]
+    return U, V, S
+
+
+def rel_frobenius_error(W, W0, s, U, V):
+    W = np.asarray(W, np.float64)
+    rec = np.asarray(s, np.float64)[:, None] * np.asarray(W0, np.float64)
+    if np.asarray(U).shape[1]:
+        rec = rec + np.asarray(U, np.float64) @ np.asarray(V, np.float64).T
+    nw = np.linalg.norm(W)
+    return float(np.linalg.norm(W - rec) / nw) if nw else float(np.linalg.norm(W - rec))
+
+
+def decompose_band(weights, rank, store=True):
+    """Decompose the member layers of one band (list of same-shape weights).
+    Returns (W0, [dict(s, U, V, err, sigma) per member])."""
+    W0 = shared_block(weights)
+    if store:
+        W0 = round_bf16(W0)
+    members = []
+    for W in weights:
+        W = np.asarray(W, np.float64)
+        s = row_scale(W, W0)
+        if store:
+            s = s.astype(np.float32).astype(np.float64)
+        U, V, S = truncated_factors(residual(W, W0, s), rank)
+        if store:
+            U, V = round_bf16(U), round_bf16(V)
+        members.append({"s": s, "U": U, "V": V, "sigma": S,
+                        "err": rel_frobenius_error(W, W0, s, U, V)})
+    return W0, members
+
+
+def decompose_family(weights, num_bands, rank, store=True):
+    """Decompose one family's per-layer weights [W_0 .. W_{L-1}] (all the
+    same shape).  Returns dict(W0={band: W0}, s=[...], U=[...], V=[...],
+    err=[...], sigma=[...]) with one s/U/V/err/sigma per layer."""
+    L = len(weights)
+    out = {"W0": {}, "s": [None] * L, "U": [None] * L, "V": [None] * L,
+           "err": [None] * L, "sigma": [None] * L}
+    for b in range(num_bands):
+        members = band_members(b, L, num_bands)
+        if not members:
+            continue
+        W0, res = decompose_band([weights[l] for l in members], rank, store)
+        out["W0"][b] = W0
+        for l, m in zip(members, res):
+            for k in ("s", "U", "V", "err", "sigma"):
+                out[k][l] = m[k]
+    return out
+
+
+def mean_error(per_family_results):
+    """Unweighted mean over every (layer, family) matrix error."""
+    errs = [e for res in per_family_results for e in res["err"] if e is not None]
+    return float(np.mean(errs))
+
+
+def eckart_young_error(W, sigma, rank):
+    """Error predicted by the discarded singular values of the residual:
+    e^2 = sum_{k > r'} sigma_k^2 / ||W||_F^2 (valid for the unrounded
+    decomposition)."""
+    r = min(rank, len(sigma))
+    return float(np.sqrt(np.sum(np.asarray(sigma[r:]) ** 2)) / np.linalg.norm(np.asarray(W, np.float64)))

@@ -1,0 +1,384 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's formula: each compares the oracle with an
+independent route (brute force, a special case with a closed form, a
+mathematical identity, a number printed on the pages).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import bf16, compare, decompose, forward, sizes
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_values(rng, shape, std=1.0):
+    return bf16.round_bf16(rng.standard_normal(shape) * std)
+
+
+# --------------------------------------------------------------------------
+# bfloat16 rounding
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("value,bits", [
+    (1.0, 0x3F80),
+    (1.0 + 2.0 ** -8, 0x3F80),                 # tie, mantissa 0 is even
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),             # tie, rounds up to the even mantissa 2
+    (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),    # just above the tie
+    (-2.5, 0xC020),
+    (0.0, 0x0000),
+    (-0.0, 0x8000),
+    (2.0 ** -130, 0x0008),                     # subnormal
+    (3.4e38, 0x7F80),                          # rounds past the bf16 maximum
+    (3.3895313892515355e38, 0x7F7F),           # bf16 maximum itself
+])
+def test_bf16_bit_patterns(value, bits):
+    assert int(bf16.bits_bf16(np.array([value]))[0]) == bits
+
+
+def test_bf16_matches_torch_rounding():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    a = np.concatenate([rng.standard_normal(50000) * 10.0 ** rng.integers(-30, 30, 50000),
+                        rng.standard_normal(1000)])
+    ours = bf16.bits_bf16(a)
+    t = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, t)
+
+
+# --------------------------------------------------------------------------
+# forward: special cases with closed forms, and the factored/explicit identity
+# --------------------------------------------------------------------------
+def test_identity_block_scales_input():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((3, 6))
+    s = np.array([2.0, -1.0, 0.5, 3.0, 1.0, 0.0])
+    y = forward.factored(x, np.eye(6), s, np.zeros((6, 0)), np.zeros((6, 0)))
+    assert np.array_equal(y, x * s[None, :])
+
+
+def test_rank_one_delta_closed_form():
+    # W0 = 0: y[t, i] = u_i * (sum_j v_j x[t, j]); N != K so a transposed V fails
+    rng = np.random.default_rng(2)
+    T, N, K = 2, 3, 5
+    x = rng.standard_normal((T, K))
+    u = rng.standard_normal(N)
+    v = rng.standard_normal(K)
+    y = forward.factored(x, np.zeros((N, K)), np.ones(N), u[:, None], v[:, None])
+    for t in range(T):
+        dot = sum(v[j] * x[t, j] for j in range(K))
+        for i in range(N):
+            assert abs(y[t, i] - u[i] * dot) <= 1e-14 * (1 + abs(u[i] * dot))
+
+
+def test_forward_brute_force_loops():
+    rng = np.random.default_rng(3)
+    T, N, K, r = 2, 4, 5, 3
+    x, W0 = rng.standard_normal((T, K)), rng.standard_normal((N, K))
+    s, U, V = rng.standard_normal(N), rng.standard_normal((N, r)), rng.standard_normal((K, r))
+    y = forward.factored(x, W0, s, U, V)
+    for t in range(T):
+        for i in range(N):
+            acc = 0.0
+            for j in range(K):
+                w = s[i] * W0[i, j]
+                for k in range(r):
+                    w += U[i, k] * V[j, k]
+                acc += w * x[t, j]
+            assert abs(y[t, i] - acc) <= 1e-12 * (1 + abs(acc))
+
+
+@pytest.mark.parametrize("T,N,K,r", [(1, 64, 48, 4), (4, 300, 200, 32), (7, 96, 512, 96)])
+def test_factored_equals_explicit(T, N, K, r):
+    """P2: the factored forward is the same map as the explicit effective
+    weight; the two differ only by rounding order (fp64)."""
+    rng = np.random.default_rng(T * 1000 + N)
+    x = bf16_values(rng, (T, K))
+    W0 = bf16_values(rng, (N, K), 1 / math.sqrt(K))
+    s = rng.normal(1, 0.05, N).astype(np.float32).astype(np.float64)
+    U, V = bf16_values(rng, (N, r), 0.02), bf16_values(rng, (K, r), 0.02)
+    yf = forward.factored(x, W0, s, U, V)
+    ye = forward.explicit(x, W0, s, U, V)
+    scale = np.abs(x) @ (np.abs(s)[:, None] * np.abs(W0) + np.abs(U) @ np.abs(V).T).T
+    assert np.all(np.abs(yf - ye) <= 1e-12 * scale + 1e-300)
+
+
+def test_stacked_is_concatenation_and_tied_slot():
+    """P7 + P8: a stacked call is its children's outputs side by side; a tied
+    child repeats the previous child's output exactly."""
+    rng = np.random.default_rng(4)
+    K = 40
+    x = bf16_values(rng, (3, K))
+    ch = []
+    for n in (24, 8, 8):
+        ch.append((bf16_values(rng, (n, K)), rng.normal(1, .05, n), bf16_values(rng, (n, 4)),
+                   bf16_values(rng, (K, 4))))
+    y = forward.stacked(x, ch)
+    assert np.array_equal(y[:, :24], forward.factored(x, *ch[0]))
+    assert np.array_equal(y[:, 24:32], forward.factored(x, *ch[1]))
+    assert np.array_equal(y[:, 32:], forward.factored(x, *ch[2]))
+    yt = forward.stacked(x, [ch[0], ch[1], "dup"])
+    assert np.array_equal(yt[:, 24:32], yt[:, 32:40])
+
+
+# --------------------------------------------------------------------------
+# decomposition
+# --------------------------------------------------------------------------
+def test_band_assignment():
+    assert [decompose.band_of(l, 26, 13) for l in range(6)] == [0, 0, 1, 1, 2, 2]
+    # Gemma 4: "5 bands (12 layers per band)" over 60 layers
+    counts = np.bincount([decompose.band_of(l, 60, 5) for l in range(60)])
+    assert list(counts) == [12] * 5
+    assert [decompose.band_of(l, 26, 26) for l in range(26)] == list(range(26))
+    assert {decompose.band_of(l, 26, 1) for l in range(26)} == {0}
+    # every band of an uneven split is contiguous and non-empty
+    b = [decompose.band_of(l, 7, 3) for l in range(7)]
+    assert b == sorted(b) and set(b) == {0, 1, 2}
+
+
+@pytest.mark.parametrize("rank", [1, 4, 32])
+def test_passthrough_is_exact(rank):
+    """P1: with one layer per band the decomposition returns the layer's own
+    weight, s = 1 and a zero delta, exactly; the factored forward then equals
+    the dense product bit for bit."""
+    rng = np.random.default_rng(rank)
+    L, N, K = 4, 48, 40
+    Ws = [bf16_values(rng, (N, K), 1 / math.sqrt(K)) for _ in range(L)]
+    res = decompose.decompose_family(Ws, num_bands=L, rank=rank, store=True)
+    x = bf16_values(rng, (5, K))
+    for l in range(L):
+        assert np.array_equal(res["W0"][l], Ws[l])
+        assert np.all(res["s"][l] == 1.0)
+        assert np.all(res["U"][l] @ res["V"][l].T == 0.0)
+        assert res["err"][l] == 0.0
+        y = forward.factored(x, res["W0"][l], res["s"][l], res["U"][l], res["V"][l])
+        assert np.array_equal(y, forward.dense(x, Ws[l]))
+
+
+@pytest.mark.parametrize("G", [1, 2, 3])
+def test_full_rank_reconstructs(G):
+    """P3: a rank of min(N, K) leaves no residual, whatever the sharing."""
+    rng = np.random.default_rng(10 + G)
+    L, N, K = 6, 20, 12
+    Ws = [rng.standard_normal((N, K)) for _ in range(L)]
+    res = decompose.decompose_family(Ws, num_bands=G, rank=min(N, K), store=False)
+    assert max(res["err"]) <= 1e-12
+    # rank above full rank is clamped to min(N, K)
+    res2 = decompose.decompose_family(Ws, num_bands=G, rank=100, store=False)
+    assert all(u.shape[1] == min(N, K) for u in res2["U"])
+
+
+@pytest.mark.parametrize("rank", [1, 5, 16])
+def test_eckart_young_tail_energy(rank):
+    """P4: the reconstructed error equals the discarded singular-value energy
+    of the residual (unrounded decomposition)."""
+    rng = np.random.default_rng(20 + rank)
+    L, N, K = 4, 40, 24
+    Ws = [rng.standard_normal((N, K)) / math.sqrt(K) for _ in range(L)]
+    res = decompose.decompose_family(Ws, num_bands=2, rank=rank, store=False)
+    for l in range(L):
+        ey = decompose.eckart_young_error(Ws[l], res["sigma"][l], rank)
+        assert abs(ey - res["err"][l]) <= 1e-10
+
+
+# ---- P5: brute force on tiny inputs -------------------------------------
+def _jacobi_eigh(A, sweeps=60):
+    """Cyclic Jacobi eigen-solver for a small symmetric matrix (pure Python
+    loops; shares nothing with LAPACK)."""
+    n = len(A)
+    a = [[float(A[i][j]) for j in range(n)] for i in range(n)]
+    v = [[1.0 if i == j else 0.0 for j in range(n)] for i in range(n)]
+    for _ in range(sweeps):
+        off = sum(a[i][j] ** 2 for i in range(n) for j in range(n) if i != j)
+        if off < 1e-300:
+            break
+        for p in range(n):
+            for q in range(p + 1, n):
+                if abs(a[p][q]) < 1e-300:
+                    continue
+                theta = (a[q][q] - a[p][p]) / (2.0 * a[p][q])
+                t = (1.0 if theta >= 0 else -1.0) / (abs(theta) + math.sqrt(theta * theta + 1.0))
+                c = 1.0 / math.sqrt(t * t + 1.0)
+                s = t * c
+                for k in range(n):
+                    akp, akq = a[k][p], a[k][q]
+                    a[k][p], a[k][q] = c * akp - s * akq, s * akp + c * akq
+                for k in range(n):
+                    apk, aqk = a[p][k], a[q][k]
+                    a[p][k], a[q][k] = c * apk - s * aqk, s * apk + c * aqk
+                for k in range(n):
+                    vkp, vkq = v[k][p], v[k][q]
+                    v[k][p], v[k][q] = c * vkp - s * vkq, s * vkp + c * vkq
+    return [a[i][i] for i in range(n)], v
+
+
+def _brute_decompose(Ws, G, rank):
+    """Band means by loops, s by bisection on the slope of the row error, the rank-r
+    residual approximation from a Jacobi eigen-decomposition of R^T R."""
+    L = len(Ws)
+    N, K = len(Ws[0]), len(Ws[0][0])
+    errs, uvs = [], []
+    for l in range(L):
+        b = (l * G) // L
+        members = [m for m in range(L) if (m * G) // L == b]
+        W0 = [[sum(Ws[m][i][j] for m in members) / len(members) for j in range(K)] for i in range(N)]
+        W = Ws[l]
+        s = []
+        for i in range(N):
+            # the row error is a convex quadratic in c; bisect on the sign of
+            # its slope, -2 * sum_j W0[i][j] * (W[i][j] - c * W0[i][j])
+            slope = lambda c: -sum(W0[i][j] * (W[i][j] - c * W0[i][j]) for j in range(K))
+            lo, hi = -50.0, 50.0
+            for _ in range(200):
+                mid = 0.5 * (lo + hi)
+                if slope(mid) > 0:
+                    hi = mid
+                else:
+                    lo = mid
+            s.append(0.5 * (lo + hi))
+        R = [[W[i][j] - s[i] * W0[i][j] for j in range(K)] for i in range(N)]
+        RtR = [[sum(R[i][p] * R[i][q] for i in range(N)) for q in range(K)] for p in range(K)]
+        lam, vec = _jacobi_eigh(RtR)
+        order = sorted(range(K), key=lambda k: -lam[k])[:min(rank, N, K)]
+        # rank-r approximation R Q_r Q_r^T
+        UVt = [[sum(R[i][m] * sum(vec[m][k] * vec[j][k] for k in order) for m in range(K))
+                for j in range(K)] for i in range(N)]
+        rec = [[s[i] * W0[i][j] + UVt[i][j] for j in range(K)] for i in range(N)]
+        num = math.sqrt(sum((W[i][j] - rec[i][j]) ** 2 for i in range(N) for j in range(K)))
+        den = math.sqrt(sum(W[i][j] ** 2 for i in range(N) for j in range(K)))
+        errs.append(num / den)
+        srt = sorted(lam, reverse=True)
+        gap = min(rank, N, K) < K and srt[min(rank, N, K) - 1] > srt[min(rank, N, K)] * (1 + 1e-6)
+        uvs.append((np.array(UVt), gap))
+    return errs, uvs
+
+
+@pytest.mark.parametrize("L,G,N,K,rank", [(4, 2, 6, 5, 2), (3, 1, 8, 8, 3), (4, 4, 5, 7, 1), (2, 1, 7, 4, 3)])
+def test_decomposition_brute_force(L, G, N, K, rank):
+    rng = np.random.default_rng(100 * L + 10 * N + K)
+    Ws = [rng.standard_normal((N, K)) for _ in range(L)]
+    res = decompose.decompose_family(Ws, num_bands=G, rank=rank, store=False)
+    errs, uvs = _brute_decompose([W.tolist() for W in Ws], G, rank)
+    assert abs(np.mean(errs) - decompose.mean_error([res])) <= 1e-10
+    for l in range(L):
+        assert abs(errs[l] - res["err"][l]) <= 1e-10
+        uv_b, gap = uvs[l]
+        if gap:
+            assert np.max(np.abs(uv_b - res["U"][l] @ res["V"][l].T)) <= 1e-9
+    # the least-squares scale is a minimum of the row error
+    for l in range(L):
+        b = decompose.band_of(l, L, G)
+        W0 = res["W0"][b]
+        for i in range(N):
+            f = lambda c: np.sum((Ws[l][i] - c * W0[i]) ** 2)
+            sv = res["s"][l][i]
+            assert f(sv) <= f(sv + 1e-6) and f(sv) <= f(sv - 1e-6)
+
+
+def test_zero_shared_row_gets_unit_scale():
+    W0 = np.zeros((2, 3))
+    W0[1] = [1.0, 2.0, 2.0]
+    s = decompose.row_scale(np.array([[1.0, 1.0, 1.0], [2.0, 4.0, 4.0]]), W0)
+    assert s[0] == 1.0 and s[1] == 2.0
+
+
+def test_sanity_band_for_unclustered_layers():
+    """P9 (a sanity band, not a pin): two independent N(0, 1/K) layers per band
+    give a pre-delta error near sqrt(1/2); a small delta lowers it a little.
+    With 26 layers in one band the error is near sqrt(25/26)."""
+    rng = np.random.default_rng(5)
+    N, K = 256, 128
+    Ws = [rng.standard_normal((N, K)) / math.sqrt(K) for _ in range(2)]
+    res0 = decompose.decompose_family(Ws, 1, 0, store=False)
+    res = decompose.decompose_family(Ws, 1, 8, store=False)
+    assert abs(np.mean(res0["err"]) - math.sqrt(0.5)) < 0.03
+    assert 0.55 < np.mean(res["err"]) < np.mean(res0["err"])
+    Ws26 = [rng.standard_normal((64, 32)) / math.sqrt(32) for _ in range(26)]
+    e26 = decompose.mean_error([decompose.decompose_family(Ws26, 1, 0, store=False)])
+    assert abs(e26 - math.sqrt(25 / 26)) < 0.03
+
+
+def test_stored_decomposition_dtypes():
+    rng = np.random.default_rng(6)
+    Ws = [bf16_values(rng, (16, 24)) for _ in range(4)]
+    res = decompose.decompose_family(Ws, 2, 3, store=True)
+    for b, W0 in res["W0"].items():
+        assert np.array_equal(bf16.round_bf16(W0), W0)
+    for l in range(4):
+        assert np.array_equal(res["s"][l].astype(np.float32).astype(np.float64), res["s"][l])
+        assert np.array_equal(bf16.round_bf16(res["U"][l]), res["U"][l])
+        assert np.array_equal(bf16.round_bf16(res["V"][l]), res["V"][l])
+
+
+# --------------------------------------------------------------------------
+# bundle sizes printed on the pages
+# --------------------------------------------------------------------------
+def _gold():
+    with open(os.path.join(GOLDEN, "bundle_sizes.json")) as f:
+        return json.load(f)
+
+
+def test_bundle_sizes_match_pages():
+    g = _gold()
+    shapes = [tuple(v) for v in g["dims"].values()]
+    L = g["num_layers"]
+    for c in g["checks"]:
+        if "value" in c:
+            mb = sizes.bundle_mb(shapes, 4, L, 1)["dense"]
+            assert abs(mb - c["value"]) <= c["tol"], c["cite"]
+        elif "percent" in c:
+            m = sizes.bundle_mb(shapes, c["rank"], L, c["G"])
+            assert abs(100 * m["theta"] / m["dense"] - c["percent"]) <= c["tol_pct"], c["cite"]
+        elif "above" in c:
+            m = sizes.bundle_mb(shapes, c["rank"], L, c["G"])
+            assert 100 * m["theta"] / m["dense"] > c["above"], c["cite"]
+        elif "share_min" in c:
+            m = sizes.bundle_mb(shapes, c["rank"], L, c["G"])
+            share = 100 * m["W0"] / m["theta"]
+            assert c["share_min"] <= share <= c["share_max"], c["cite"]
+        elif "below" in c:
+            for r in c["ranks"]:
+                m = sizes.bundle_mb(shapes, r, L, c["G"])
+                assert 100 * m["theta"] / m["dense"] < c["below"], c["cite"]
+        else:
+            ms = [sizes.bundle_mb(shapes, r, L, c["G"]) for r in c["ranks"]]
+            assert len({round(m["W0"], 6) for m in ms}) == 1 and len({round(m["s"], 6) for m in ms}) == 1
+            assert ms[0]["U"] < ms[1]["U"] < ms[2]["U"]
+
+
+def test_bundle_size_closed_forms():
+    """The element counts behind the page's table (derived by hand)."""
+    shapes = [tuple(v) for v in _gold()["dims"].values()]
+    c = sizes.bundle_counts(shapes, 32, 26, 1)
+    assert c["dense"] == 444_727_296
+    assert c["W0"] == 17_104_896
+    assert c["s"] == 26 * 12_032 and c["U"] == 26 * 12_032 * 32 and c["V"] == 26 * 10_880 * 32
+    m = sizes.bundle_mb(shapes, 32, 26, 1)
+    assert abs(100 * m["W0"] / m["theta"] - 46.9) < 0.05
+
+
+# --------------------------------------------------------------------------
+# tolerance checker
+# --------------------------------------------------------------------------
+def test_compare_accepts_and_rejects():
+    rng = np.random.default_rng(8)
+    y = rng.standard_normal((4, 100))
+    assert compare.compare(y, y)["ok"]
+    assert compare.compare(y * (1 + 1e-3), y)["ok"]
+    assert not compare.compare(y * (1 + 1e-2), y)["ok"]           # row error 1e-2 > 5e-3
+    bad = y.copy()
+    bad[2, 7] += 0.2 * np.abs(y).max()
+    assert not compare.compare(bad, y)["ok"]                      # one large element
+    z = y.copy()
+    z[1] = 0.0
+    assert compare.compare(z, z)["ok"]
+    w = z.copy()
+    w[1, 3] = 1e-6
+    assert not compare.compare(w, z)["ok"]                        # zero row must match exactly
+    assert not compare.compare(y[:, :50], y)["ok"]
+    nan = y.copy()
+    nan[0, 0] = np.nan
+    assert not compare.compare(nan, y)["ok"]
