@@ -1,0 +1,180 @@
+/*
+ * weightless.h -- C ABI of the weightless linear on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages "Add a new model architecture", introduction, and
+ * "Quality (Gemma 4 31B)", section "Kernel optimizations"): every dense
+ * projection weight of a decoder layer is replaced by a theta bundle -- a
+ * block W0 shared by a band of layers, a per-row scale s, and a rank-r delta
+ * (U, V) -- and the projection of activations x is evaluated as
+ *
+ *     y = s (.) (W0 x) + U (V^T x)
+ *
+ * with the q/k/v (and gate/up) projections of one layer fused into a single
+ * stacked call over their shared x.
+ *
+ * Conventions for every entry point
+ *   - Row-major storage, tokens are rows: x [T, K], y [T, N] (N output rows of
+ *     the projection become the columns of y), W0 [N, K], s [N], U [N, r],
+ *     V [K, r].
+ *   - bf16 = IEEE bfloat16 (raw 16-bit patterns); s is float32.  Arithmetic
+ *     accumulates in float32; y is rounded to bf16, nearest-even.
+ *   - Every function returns a wl_status (0 on success).  Argument errors are
+ *     detected on the host and returned before anything is enqueued;
+ *     wl_last_error() then describes the failure (thread-local string).
+ *   - Device work is only enqueued on the given HIP stream (a hipStream_t
+ *     passed as void*, NULL = the null stream); no entry point synchronizes
+ *     unless its comment says so.  Device faults surface at the caller's next
+ *     synchronization, as for any HIP launch.
+ *   - The caller owns all device memory (arena, x, y, workspace).  The
+ *     library never allocates device memory.
+ */
+#ifndef WEIGHTLESS_H
+#define WEIGHTLESS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WL_OK = 0,
+  WL_EINVAL = -1,   /* bad pointer, index, kind or duplicate/missing source */
+  WL_ESHAPE = -2,   /* dimension not allowed (K % 8 != 0, rank > min(N, K), ...) */
+  WL_EDTYPE = -3,   /* a source tensor is not in its required dtype */
+  WL_ERANGE = -4,   /* layer or family out of range, or family absent */
+  WL_ENOSPACE = -5, /* arena or workspace smaller than required */
+  WL_EHIP = -6      /* a HIP runtime call failed (message has the HIP error) */
+} wl_status;
+
+/* The seven projection families of a decoder layer ("Add the weightless
+ * fields" section: q_proj, k_proj, v_proj, o_proj, gate_proj, up_proj,
+ * down_proj). */
+typedef enum { WL_Q = 0, WL_K = 1, WL_V = 2, WL_O = 3, WL_GATE = 4, WL_UP = 5, WL_DOWN = 6 } wl_family;
+#define WL_NUM_FAMILIES 7
+
+/* Stacked calls over one shared x ("Kernel optimizations > GEMM path":
+ * q/k/v batched into one call).  Output children are concatenated along N in
+ * the order q, k, v (resp. gate, up). */
+typedef enum { WL_STACK_QKV = 0, WL_STACK_GATE_UP = 1 } wl_stack;
+
+typedef enum { WL_DTYPE_BF16 = 0, WL_DTYPE_F32 = 1 } wl_dtype;
+typedef enum { WL_SRC_W0 = 0, WL_SRC_S = 1, WL_SRC_U = 2, WL_SRC_V = 3 } wl_src_kind;
+
+#define WL_MAX_LAYER_TYPES 2
+
+/* Shape of a theta bundle.
+ *  num_layers L, num_bands G (G = the pages' shared_blocks, "Add the weightless
+ *    fields"): layer l belongs to band floor(l * G / L) -- contiguous, balanced
+ *    bands; 1 <= G <= L.  G = L gives one layer per band (passthrough).
+ *  num_layer_types 1 (uniform attention) or 2 (mixed attention: e.g. 0 =
+ *    sliding, 1 = full; "Decompose HF weights: the mixed-attention case").
+ *  layer_type [L] with values < num_layer_types, or NULL for all type 0.
+ *    The array is copied; the caller may free it after theta_bundle_load.
+ *  out_dim/in_dim/rank [type][family]: N, K and r.  out_dim 0 means the family
+ *    is absent on that type.  K % 8 == 0 is required; 0 <= r <= min(N, K).
+ *  k_eq_v_type_mask: bit t set means layers of type t carry no v bundle and
+ *    their v projection reuses k's (attention_k_eq_v).
+ *  W0 grouping: attention families (q, k, v, o) have one W0 per
+ *    (band, layer type, family); MLP families (gate, up, down) one W0 per
+ *    (band, family) shared by both layer types, so their out/in dims must agree
+ *    across types.  W0 exists only for (band, type) pairs that hold a layer. */
+typedef struct {
+  int32_t num_layers;
+  int32_t num_bands;
+  int32_t num_layer_types;
+  const int8_t *layer_type;
+  int32_t out_dim[WL_MAX_LAYER_TYPES][WL_NUM_FAMILIES];
+  int32_t in_dim[WL_MAX_LAYER_TYPES][WL_NUM_FAMILIES];
+  int32_t rank[WL_MAX_LAYER_TYPES][WL_NUM_FAMILIES];
+  uint32_t k_eq_v_type_mask;
+} wl_bundle_spec;
+
+/* One source tensor handed to theta_bundle_load.
+ *  kind W0: index = band, layer_type = type (0 for MLP families), bf16 [N, K]
+ *  kind S:  index = layer, float32 [N]
+ *  kind U:  index = layer, bf16 [N, r]
+ *  kind V:  index = layer, bf16 [K, r]   (V, not V^T: y = U (V^T x))
+ *  on_device != 0: ptr is device memory (copied on the stream);
+ *  on_device == 0: ptr is host memory (copied before theta_bundle_load returns). */
+typedef struct {
+  int32_t kind;
+  int32_t index;
+  int32_t layer_type;
+  int32_t family;
+  int32_t dtype;
+  int32_t on_device;
+  const void *ptr;
+} wl_src;
+
+typedef struct wl_bundle wl_bundle; /* opaque; host metadata only */
+
+/* Bytes of device arena that theta_bundle_load needs for this spec (0 if the
+ * spec is invalid; wl_last_error() then says why).  The arena holds, 256-byte
+ * aligned, each W0 once -- stacked groups [q;k;v] and [gate;up] with their
+ * rows contiguous -- and per layer its s (float32), U (bf16, rows padded to a
+ * multiple of 8 ranks) and V^T (bf16 [r, K], ranks padded to a multiple of 8). */
+size_t theta_bundle_arena_bytes(const wl_bundle_spec *spec);
+
+/* Pack a theta bundle into the caller's device arena (d_arena, 256-byte
+ * aligned, at least theta_bundle_arena_bytes(spec) bytes) on `stream`.
+ * Every source the spec implies must appear exactly once in srcs[0..n_src);
+ * any other source is an error.  The library never decomposes: sources are
+ * already-decomposed bundles.  Device sources may be reused or freed once the
+ * stream has passed this point; host sources as soon as the call returns.
+ * On success *out receives a handle that refers to the arena (not owning it). */
+wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size_t n_src,
+                            void *d_arena, size_t arena_bytes, void *stream, wl_bundle **out);
+
+/* Free the host handle (never the arena).  NULL is accepted. */
+wl_status theta_bundle_free(wl_bundle *bundle);
+
+/* Workspace bytes needed by any weightless_linear / weightless_stacked_linear
+ * call on this bundle with T tokens (T <= 16: decode path; T > 16: prefill
+ * path).  0 with wl_last_error() set on error. */
+size_t weightless_workspace_bytes(const wl_bundle *bundle, int32_t T);
+
+/* Prepare a workspace for first use: enqueues a fill of d_ws with zeros on
+ * `stream` (a kernel, not a memset node).  Calls leave the workspace's
+ * synchronization words at zero when they finish, so this is needed once per
+ * workspace, not per call. */
+wl_status weightless_workspace_init(void *d_ws, size_t ws_bytes, void *stream);
+
+/* Copy the workspace's sticky error word to *out (0 = no device-side error;
+ * bit 0 = a decode launch gave up waiting for its V^T x reduction).
+ * This call synchronizes `stream`. */
+wl_status weightless_workspace_error(const void *d_ws, void *stream, uint32_t *out);
+
+/* y = s (.) (W0 x) + U (V^T x) for one family of one layer.
+ *  d_x bf16 [T, K], d_y bf16 [T, N] (must not alias d_x), T >= 0 (T = 0: no-op).
+ *  T <= 16 runs the decode kernel (one launch), T > 16 the prefill MFMA GEMMs
+ *  (two launches: Z = X V, then Y = (X W0^T) (.) s + Z U^T).
+ *  family WL_V on a K=V-tied layer type evaluates k's bundle.
+ *  d_ws: workspace of at least weightless_workspace_bytes(bundle, T) bytes,
+ *  initialized once with weightless_workspace_init; concurrent calls need
+ *  distinct workspaces. */
+wl_status weightless_linear(const wl_bundle *bundle, int32_t layer, int32_t family,
+                            const void *d_x, int32_t T, void *d_y,
+                            void *d_ws, size_t ws_bytes, void *stream);
+
+/* The stacked call: q|k|v (or gate|up) of one layer over one x in a single
+ * decode launch (two for prefill).  d_y bf16 [T, N_q + N_k + N_v] (resp.
+ * [T, N_gate + N_up]).  On a K=V-tied layer type the v slot receives a copy of
+ * k's output, so the output layout is the same on every layer. */
+wl_status weightless_stacked_linear(const wl_bundle *bundle, int32_t layer, int32_t stack,
+                                    const void *d_x, int32_t T, void *d_y,
+                                    void *d_ws, size_t ws_bytes, void *stream);
+
+/* Output width N of a single-family call, or of a stacked call (stack >= 0
+ * with family < 0); 0 on error.  Host-only. */
+int32_t weightless_out_dim(const wl_bundle *bundle, int32_t layer, int32_t family, int32_t stack);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char *wl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WEIGHTLESS_H */

@@ -8,6 +8,8 @@ Decomposed workloads run ``decompose.decompose_band`` on the seeded per-layer
 weights of the band (and layer type) the layer belongs to.  With K=V tying,
 v has no bundle and its output is k's.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from . import forward
@@ -22,10 +24,52 @@ def to64(t):
 
 
 class OracleWorkload:
-    def __init__(self, wl, device="cpu"):
+    def __init__(self, wl, device="cpu", cache_w0=4):
         self.wl = wl
         self.device = device
         self._dec = {}
+        self._w0 = {}
+        self._cache_w0 = cache_w0
+
+    def w0(self, band, ltype, fam):
+        key = (band, ltype if fam in ("q", "k", "v", "o") else 0, fam)
+        if key not in self._w0:
+            if len(self._w0) >= self._cache_w0:
+                self._w0.pop(next(iter(self._w0)))
+            self._w0[key] = to64(self.wl.w0(band, ltype, fam, self.device))
+        return self._w0[key]
+
+    def prefetch_decompositions(self, keys, workers=8):
+        """Decompose several (band, layer type, family) groups concurrently.
+        Each decomposition is the same sequential computation as
+        ``decomposed_band``; only the scheduling is parallel (LAPACK releases
+        the GIL; each thread's BLAS is limited to one core)."""
+        todo = [k for k in keys if k not in self._dec]
+        if not todo:
+            return
+        wl = self.wl
+        inputs = {}
+        for (b, t, f) in todo:
+            members = [l for l in band_members(b, wl.num_layers, wl.num_bands) if wl.layer_types[l] == t]
+            inputs[(b, t, f)] = (members, [to64(wl.layer_weight(l, f, self.device)) for l in members])
+
+        def work(key):
+            members, Ws = inputs[key]
+            W0, res = decompose_band(Ws, wl.rank, store=True)
+            return key, (W0, dict(zip(members, res)))
+
+        try:
+            from threadpoolctl import threadpool_limits
+            limiter = threadpool_limits(1)
+        except Exception:  # pragma: no cover
+            limiter = None
+        try:
+            with ThreadPoolExecutor(workers) as ex:
+                for key, val in ex.map(work, todo):
+                    self._dec[key] = val
+        finally:
+            if limiter is not None:
+                limiter.restore_original_limits()
 
     def _tied(self, layer, fam):
         return fam == "v" and self.wl.layer_types[layer] in self.wl.k_eq_v_types
@@ -51,7 +95,7 @@ class OracleWorkload:
             W0, per = self.decomposed_band(wl.band(layer), lt, fam)
             m = per[layer]
             return W0, m["s"], m["U"], m["V"]
-        return (to64(wl.w0(wl.band(layer), lt, fam, self.device)), to64(wl.s(layer, fam, self.device)),
+        return (self.w0(wl.band(layer), lt, fam), to64(wl.s(layer, fam, self.device)),
                 to64(wl.u(layer, fam, self.device)), to64(wl.v(layer, fam, self.device)))
 
     def families_of(self, layer, call):

@@ -1,0 +1,163 @@
+"""GPU edge cases through the C ABI: ragged shapes (row tails, K tails, rank
+padding, children straddling tiles), K=V tying, stacked versus single calls,
+run-to-run determinism, rank 0, T = 0, workspace errors, host-resident
+sources and graph replay."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import synth.device as sdev
+from oracle.compare import compare
+from oracle.workload import OracleWorkload
+from weight_shared_rank_amd import binding
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def announce(msg):
+    sys.__stderr__.write(f"[gpu] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def np64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def ragged(rank=5, layer_types=(0, 0, 0), k_eq_v=(), bands=2):
+    dims = {}
+    for t in sorted(set(layer_types)):
+        q = 200 if t == 0 else 136
+        dims.update({(t, "q"): (q, 264), (t, "k"): (72, 264), (t, "v"): (72, 264), (t, "o"): (264, q),
+                     (t, "gate"): (300, 264), (t, "up"): (300, 264), (t, "down"): (264, 296)})
+    return synth.custom(len(layer_types), bands, rank, dims, layer_types=layer_types, k_eq_v_types=k_eq_v,
+                        cid=50 + rank)
+
+
+def call(b, layer, c, x):
+    return b.stacked(layer, c, x) if c in ("qkv", "gate_up") else b.linear(layer, c, x)
+
+
+@pytest.mark.parametrize("rank", [0, 5, 64])
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 40])
+def test_ragged_shapes(gpu_lib, rank, T):
+    wl = ragged(rank)
+    ow = OracleWorkload(wl, DEV)
+    b = sdev.load(wl, DEV)
+    for layer in range(wl.num_layers):
+        for c in ["qkv", "o", "gate_up", "down"] + list(synth.FAMILIES):
+            x = wl.x(layer, c, T, DEV)
+            announce(f"ragged r={rank} T={T} layer {layer} {c}")
+            y = call(b, layer, c, x)
+            torch.cuda.synchronize()
+            res = compare(np64(y), ow.call(layer, c, np64(x)))
+            assert res["ok"], f"layer {layer} {c}: {res}"
+
+
+@pytest.mark.parametrize("T", [1, 16, 33])
+def test_stacked_equals_singles_bitwise(gpu_lib, T):
+    wl = ragged(7)
+    b = sdev.load(wl, DEV)
+    for layer in range(wl.num_layers):
+        for c, fams in (("qkv", ("q", "k", "v")), ("gate_up", ("gate", "up"))):
+            x = wl.x(layer, c, T, DEV)
+            announce(f"stacked vs singles T={T} layer {layer} {c}")
+            ys = b.stacked(layer, c, x)
+            cat = torch.cat([b.linear(layer, f, x) for f in fams], dim=1)
+            torch.cuda.synchronize()
+            assert torch.equal(ys.float(), cat.float()), f"layer {layer} {c} T={T}"
+
+
+@pytest.mark.parametrize("T", [1, 16, 24])
+def test_k_eq_v_mixed_types(gpu_lib, T):
+    wl = ragged(6, layer_types=(0, 1, 0, 1), k_eq_v=(1,), bands=2)
+    ow = OracleWorkload(wl, DEV)
+    b = sdev.load(wl, DEV)
+    for layer in range(4):
+        x = wl.x(layer, "qkv", T, DEV)
+        announce(f"k_eq_v T={T} layer {layer}")
+        y = b.stacked(layer, "qkv", x)
+        yv = b.linear(layer, "v", x)
+        yk = b.linear(layer, "k", x)
+        torch.cuda.synchronize()
+        assert compare(np64(y), ow.call(layer, "qkv", np64(x)))["ok"]
+        nq, nk = wl.shape(wl.layer_types[layer], "q")[0], 72
+        if wl.layer_types[layer] == 1:
+            assert torch.equal(y[:, nq:nq + nk], y[:, nq + nk:])
+            assert torch.equal(yv, yk)
+        assert y.shape[1] == nq + 2 * nk
+
+
+def test_determinism_and_t0(gpu_lib):
+    wl = synth.workload(1)
+    b = sdev.load(wl, DEV)
+    for T in (4, 16, 200):
+        x = wl.x(0, "up", T, DEV)
+        announce(f"determinism T={T}")
+        y1 = b.linear(0, "up", x)
+        y2 = b.linear(0, "up", x)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+    y = torch.full((0, 4096), 7, dtype=torch.bfloat16, device=DEV)
+    b.linear(0, "up", torch.empty((0, 1152), dtype=torch.bfloat16, device=DEV), y=y)
+
+
+def test_workspace_too_small_and_aliasing(gpu_lib):
+    wl = synth.workload(1)
+    b = sdev.load(wl, DEV)
+    x = wl.x(0, "up", 4, DEV)
+    small = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(binding.WlError) as e:
+        b.linear(0, "up", x, ws=small)
+    assert e.value.status == -5
+    big = torch.empty((4, 4096 + 1152), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(binding.WlError) as e:
+        b.linear(0, "up", big[:, :1152].contiguous(), y=None)  # fine: separate buffers
+        b.linear(0, "up", big.view(-1)[:4 * 1152].view(4, 1152), y=big.view(-1)[1000:1000 + 4 * 4096].view(4, 4096))
+    assert e.value.status == -1
+
+
+def test_host_sources_match_device_sources(gpu_lib):
+    wl = ragged(5)
+    bd = sdev.load(wl, DEV)
+    bh = binding.ThetaBundle(sdev.spec_of(wl), [(k, i, t, f, v.cpu()) for (k, i, t, f, v) in sdev.sources_of(wl, DEV)])
+    for T in (3, 20):
+        x = wl.x(2, "qkv", T, DEV)
+        announce(f"host sources T={T}")
+        assert torch.equal(bd.stacked(2, "qkv", x), bh.stacked(2, "qkv", x))
+
+
+def test_graph_replay(gpu_lib):
+    """Decode launches leave their synchronization words at zero, so a captured
+    graph replays correctly; checked on several replays with eager work and
+    synchronizations in between."""
+    wl = ragged(9)
+    b = sdev.load(wl, DEV)
+    xs = wl.x(1, "qkv", 3, DEV)
+    xp = wl.x(1, "gate_up", 40, DEV)
+    ref_s = b.stacked(1, "qkv", xs)
+    ref_p = b.stacked(1, "gate_up", xp)
+    torch.cuda.synchronize()
+    ys = torch.empty_like(ref_s)
+    yp = torch.empty_like(ref_p)
+    ws_d = b.workspace(3)
+    ws_p = b.workspace(40)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        b.stacked(1, "qkv", xs, y=ys, ws=ws_d)
+        b.stacked(1, "gate_up", xp, y=yp, ws=ws_p)
+    for rep in range(5):
+        announce(f"graph replay {rep}")
+        ys.zero_()
+        yp.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys, ref_s) and torch.equal(yp, ref_p), f"replay {rep}"
+        b.stacked(1, "qkv", xs)       # eager work between replays
+        torch.cuda.synchronize()
+    assert b.workspace_error(ws_d) == 0

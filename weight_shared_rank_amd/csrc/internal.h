@@ -1,0 +1,62 @@
+// Internal declarations shared by the host side of the library and its HIP
+// kernels.  Not part of the public ABI (include/weightless.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wl {
+
+// Decode path limit: T <= kDecodeMaxT tokens run the one-launch decode kernel.
+constexpr int kDecodeMaxT = 16;
+constexpr int kMaxChildren = 3;
+
+// Workspace header words (uint32 each, at the start of the workspace).
+enum CtrlWord { kCtrlError = 0, kCtrlZReady = 1, kCtrlDone = 2 };
+constexpr size_t kCtrlBytes = 256;
+constexpr uint32_t kErrZWaitTimeout = 1u;
+
+// One child projection of a (possibly stacked) call, as the kernels see it.
+struct ChildDesc {
+  const uint16_t *U;   // [N, rpad] bf16, row-major (padded ranks are zero)
+  int32_t row_start;   // first row of this child among the call's rows
+  int32_t N;           // rows of this child
+  int32_t rpad;        // rank rounded up to a multiple of 8 (U row stride)
+  int32_t zoff;        // first V^T row / z column of this child
+  int32_t y_off;       // first output column of this child in y
+  int32_t dup_off;     // second output column offset (K=V tying) or -1
+};
+
+// One call: rows [0, Ntot) of W0 and s, ranks [0, Rz) of V^T and z.
+struct CallDesc {
+  const uint16_t *x;   // [T, K] bf16
+  const uint16_t *W0;  // [Ntot, K] bf16
+  const float *s;      // [Ntot]
+  const uint16_t *Vt;  // [Rz, K] bf16
+  uint16_t *y;         // [T, ldy] bf16
+  int32_t T, K, Ntot, Rz, ldy;
+  int32_t nchild;
+  ChildDesc ch[kMaxChildren];
+};
+
+// Decode-path kernel launch (T <= 16): one launch computes z = V^T x, the
+// shared-block product and the fused epilogue.
+struct DecodeWs {
+  uint32_t *ctrl;      // workspace header
+  uint16_t *zhi;       // [16, ldz] bf16: z rounded to bf16
+  uint16_t *zlo;       // [16, ldz] bf16: z - zhi rounded to bf16
+  int32_t ldz;
+};
+hipError_t launch_decode(const CallDesc &c, const DecodeWs &ws, hipStream_t stream);
+
+// Prefill path (T > 16): Z = X V into zbuf [T, Rz] bf16, then the main GEMM
+// with the scale and rank-r epilogue.
+hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, hipStream_t stream);
+
+// Load-time helpers.
+hipError_t launch_fill_zero(void *dst, size_t bytes, hipStream_t stream);
+// V [K, r] (row-major, bf16) -> V^T rows [r, K] at dst (row stride K).
+hipError_t launch_transpose_v(const uint16_t *V, int32_t K, int32_t r, uint16_t *dst,
+                              hipStream_t stream);
+
+}  // namespace wl

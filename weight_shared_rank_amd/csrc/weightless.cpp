@@ -1,0 +1,534 @@
+// Host side of the weightless linear library: theta-bundle spec validation,
+// arena layout, bundle loading and call dispatch (include/weightless.h).
+//
+// Arena layout (all offsets 256-byte aligned), following the pages' ownership
+// model -- W0 declared once per band at model level and injected into every
+// layer of the band ("Add a new model architecture" page, "Swap in the
+// weightless layers"), grouped per (band, layer type, family) for attention
+// and per (band, family) for the MLP ("Decompose HF weights: the
+// mixed-attention case"):
+//
+//   for each band b, layer-type key t, group g in {QKV, O, GATE_UP, DOWN}
+//   that some layer of the band uses:
+//       W0 group block [sum of child N, K] bf16 -- children's rows
+//       concatenated (q;k;v, gate;up), so a stacked call streams one block
+//   for each layer l, group g present on l's type:
+//       s   [sum N]          float32
+//       V^T [sum rpad, K]    bf16   (child ranks padded to a multiple of 8
+//                                    with zero rows)
+//       U   [N, rpad]        bf16, one block per child (zero pad columns)
+//
+// A stacked call therefore sees contiguous W0 rows, contiguous s, contiguous
+// V^T rows and one U block per child; a single-family call sees a row slice.
+#include <hip/hip_runtime.h>
+
+#include <array>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "weightless.h"
+
+namespace {
+
+constexpr int kGroups = 4;
+enum { G_QKV = 0, G_O = 1, G_GATEUP = 2, G_DOWN = 3 };
+constexpr int kGroupOf[WL_NUM_FAMILIES] = {G_QKV, G_QKV, G_QKV, G_O, G_GATEUP, G_GATEUP, G_DOWN};
+constexpr int kGroupFams[kGroups][3] = {{WL_Q, WL_K, WL_V}, {WL_O, -1, -1}, {WL_GATE, WL_UP, -1}, {WL_DOWN, -1, -1}};
+constexpr int kGroupNFam[kGroups] = {3, 1, 2, 1};
+constexpr int32_t kMaxDim = 1 << 20;
+
+inline bool is_mlp_group(int g) { return g >= G_GATEUP; }
+inline bool is_mlp_family(int f) { return f >= WL_GATE; }
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+thread_local std::string g_err;
+
+wl_status fail(wl_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+wl_status hip_fail(hipError_t e, const char *what) {
+  return fail(WL_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct GroupShape {
+  bool any = false;
+  bool tied = false;  // QKV group on a K=V-tied type: the v slot copies k
+  int K = 0;
+  int nchild = 0;
+  int fam[3] = {-1, -1, -1};
+  int N[3] = {0, 0, 0};
+  int r[3] = {0, 0, 0};
+  int rpad[3] = {0, 0, 0};
+  int row_start[3] = {0, 0, 0};
+  int zoff[3] = {0, 0, 0};
+  int Ntot = 0;
+  int Rtot = 0;
+  int child_of_fam[WL_NUM_FAMILIES] = {-1, -1, -1, -1, -1, -1, -1};
+};
+
+struct LayerOff {
+  int64_t s[kGroups];
+  int64_t vt[kGroups];
+  int64_t u[kGroups][3];
+};
+
+struct Layout {
+  int L = 0, G = 0, NT = 0;
+  std::vector<int8_t> ltype;
+  uint32_t tied_mask = 0;
+  GroupShape gs[WL_MAX_LAYER_TYPES][kGroups];
+  std::vector<int64_t> w0;  // [(band * NT + tkey) * kGroups + g], -1 if absent
+  std::vector<LayerOff> lay;
+  size_t bytes = 0;
+  int Rmax = 0;
+
+  int band(int l) const { return static_cast<int>((static_cast<int64_t>(l) * G) / L); }
+  int64_t &w0_at(int b, int t, int g) { return w0[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
+  int64_t w0_at(int b, int t, int g) const { return w0[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
+};
+
+bool tied(const Layout &lo, int t) { return (lo.tied_mask >> t) & 1u; }
+
+// Validate the spec and compute the arena layout.
+wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
+  if (!spec) return fail(WL_EINVAL, "spec is NULL");
+  const int L = spec->num_layers, G = spec->num_bands, NT = spec->num_layer_types;
+  if (L < 1 || L > kMaxDim) return fail(WL_EINVAL, "num_layers %d out of range", L);
+  if (G < 1 || G > L) return fail(WL_EINVAL, "num_bands %d must be in [1, num_layers=%d]", G, L);
+  if (NT < 1 || NT > WL_MAX_LAYER_TYPES) return fail(WL_EINVAL, "num_layer_types %d must be 1 or 2", NT);
+  if (spec->k_eq_v_type_mask >> NT) return fail(WL_EINVAL, "k_eq_v_type_mask 0x%x names a layer type >= %d", spec->k_eq_v_type_mask, NT);
+  lo.L = L;
+  lo.G = G;
+  lo.NT = NT;
+  lo.tied_mask = spec->k_eq_v_type_mask;
+  lo.ltype.assign(L, 0);
+  if (spec->layer_type) {
+    for (int l = 0; l < L; ++l) {
+      if (spec->layer_type[l] < 0 || spec->layer_type[l] >= NT)
+        return fail(WL_EINVAL, "layer_type[%d] = %d out of range", l, spec->layer_type[l]);
+      lo.ltype[l] = spec->layer_type[l];
+    }
+  }
+  for (int t = 0; t < NT; ++t) {
+    for (int f = 0; f < WL_NUM_FAMILIES; ++f) {
+      if (f == WL_V && tied(lo, t)) continue;
+      const int N = spec->out_dim[t][f], K = spec->in_dim[t][f], r = spec->rank[t][f];
+      if (N < 0 || N > kMaxDim) return fail(WL_ESHAPE, "out_dim[%d][%d] = %d out of range", t, f, N);
+      if (N == 0) continue;
+      if (K <= 0 || K > kMaxDim) return fail(WL_ESHAPE, "in_dim[%d][%d] = %d out of range", t, f, K);
+      if (K % 8) return fail(WL_ESHAPE, "in_dim[%d][%d] = %d is not a multiple of 8", t, f, K);
+      if (r < 0 || r > N || r > K) return fail(WL_ESHAPE, "rank[%d][%d] = %d outside [0, min(N=%d, K=%d)]", t, f, r, N, K);
+    }
+    if (tied(lo, t) && spec->out_dim[t][WL_K] == 0)
+      return fail(WL_ESHAPE, "layer type %d ties v to k but has no k", t);
+  }
+  if (NT == 2) {
+    for (int f = WL_GATE; f <= WL_DOWN; ++f)
+      if (spec->out_dim[0][f] != spec->out_dim[1][f] || (spec->out_dim[0][f] && spec->in_dim[0][f] != spec->in_dim[1][f]))
+        return fail(WL_ESHAPE, "MLP family %d shares W0 across layer types but its shape differs between them", f);
+  }
+  // Group shapes per layer type.
+  lo.Rmax = 0;
+  for (int t = 0; t < NT; ++t) {
+    for (int g = 0; g < kGroups; ++g) {
+      GroupShape &gs = lo.gs[t][g];
+      gs = GroupShape();
+      for (int i = 0; i < kGroupNFam[g]; ++i) {
+        const int f = kGroupFams[g][i];
+        if (f == WL_V && tied(lo, t)) {
+          gs.tied = true;
+          continue;
+        }
+        const int N = spec->out_dim[t][f];
+        if (N == 0) continue;
+        const int K = spec->in_dim[t][f];
+        if (gs.nchild > 0 && K != gs.K)
+          return fail(WL_ESHAPE, "families of one stacked group need one in_dim (type %d family %d: %d vs %d)", t, f, K, gs.K);
+        const int c = gs.nchild++;
+        gs.K = K;
+        gs.fam[c] = f;
+        gs.N[c] = N;
+        gs.r[c] = spec->rank[t][f];
+        gs.rpad[c] = (gs.r[c] + 7) & ~7;
+        gs.row_start[c] = gs.Ntot;
+        gs.zoff[c] = gs.Rtot;
+        gs.Ntot += N;
+        gs.Rtot += gs.rpad[c];
+        gs.child_of_fam[f] = c;
+        gs.any = true;
+      }
+      if (!gs.any) gs.tied = false;
+      if (gs.Rtot > lo.Rmax) lo.Rmax = gs.Rtot;
+    }
+  }
+  // W0 regions: one per (band, type key, group) used by some layer.
+  size_t off = 0;
+  lo.w0.assign(static_cast<size_t>(G) * NT * kGroups, -1);
+  for (int b = 0; b < G; ++b) {
+    for (int t = 0; t < NT; ++t) {
+      for (int g = 0; g < kGroups; ++g) {
+        if (is_mlp_group(g) && t != 0) continue;
+        bool used = false;
+        for (int l = 0; l < L && !used; ++l)
+          if (lo.band(l) == b && (is_mlp_group(g) || lo.ltype[l] == t) && lo.gs[lo.ltype[l]][g].any) used = true;
+        if (!used) continue;
+        const GroupShape &gs = lo.gs[t][g];
+        lo.w0_at(b, t, g) = static_cast<int64_t>(off);
+        off = align256(off + static_cast<size_t>(gs.Ntot) * gs.K * 2);
+      }
+    }
+  }
+  lo.lay.resize(L);
+  for (int l = 0; l < L; ++l) {
+    LayerOff &lf = lo.lay[l];
+    const int t = lo.ltype[l];
+    for (int g = 0; g < kGroups; ++g) {
+      lf.s[g] = lf.vt[g] = -1;
+      for (int c = 0; c < 3; ++c) lf.u[g][c] = -1;
+      const GroupShape &gs = lo.gs[t][g];
+      if (!gs.any) continue;
+      lf.s[g] = static_cast<int64_t>(off);
+      off = align256(off + static_cast<size_t>(gs.Ntot) * 4);
+      lf.vt[g] = static_cast<int64_t>(off);
+      off = align256(off + static_cast<size_t>(gs.Rtot) * gs.K * 2);
+      for (int c = 0; c < gs.nchild; ++c) {
+        lf.u[g][c] = static_cast<int64_t>(off);
+        off = align256(off + static_cast<size_t>(gs.N[c]) * gs.rpad[c] * 2);
+      }
+    }
+  }
+  lo.bytes = off;
+  return WL_OK;
+}
+
+size_t ws_bytes_for(const Layout &lo, int32_t T) {
+  const size_t zb = align256(static_cast<size_t>(wl::kDecodeMaxT) * lo.Rmax * 2);
+  size_t n = wl::kCtrlBytes + 2 * zb;
+  if (T > wl::kDecodeMaxT) n += align256(static_cast<size_t>(T) * lo.Rmax * 2);
+  return n;
+}
+
+}  // namespace
+
+struct wl_bundle {
+  Layout lo;
+  uint8_t *arena = nullptr;
+  size_t arena_bytes = 0;
+};
+
+namespace {
+
+struct Resolved {
+  wl::CallDesc c;
+  int out_dim;
+};
+
+// Fill a CallDesc for (layer, family) or (layer, stack).
+wl_status resolve(const wl_bundle *h, int32_t layer, int32_t family, int32_t stack, Resolved &rv) {
+  if (!h) return fail(WL_EINVAL, "bundle is NULL");
+  const Layout &lo = h->lo;
+  if (layer < 0 || layer >= lo.L) return fail(WL_ERANGE, "layer %d outside [0, %d)", layer, lo.L);
+  const int t = lo.ltype[layer];
+  const int b = lo.band(layer);
+  int g;
+  int first = 0, last = 0;  // children range [first, last)
+  const bool single = stack < 0;
+  if (single) {
+    if (family < 0 || family >= WL_NUM_FAMILIES) return fail(WL_ERANGE, "family %d out of range", family);
+    int f = family;
+    if (f == WL_V && tied(lo, t)) f = WL_K;
+    g = kGroupOf[f];
+    const int c = lo.gs[t][g].child_of_fam[f];
+    if (c < 0) return fail(WL_ERANGE, "family %d is absent on layer %d (type %d)", family, layer, t);
+    first = c;
+    last = c + 1;
+  } else {
+    if (stack != WL_STACK_QKV && stack != WL_STACK_GATE_UP) return fail(WL_ERANGE, "stack %d out of range", stack);
+    g = stack == WL_STACK_QKV ? G_QKV : G_GATEUP;
+    const GroupShape &gs = lo.gs[t][g];
+    const int need = stack == WL_STACK_QKV ? (gs.tied ? 2 : 3) : 2;
+    if (gs.nchild != need)
+      return fail(WL_ERANGE, "stacked call %d needs all of its families on layer %d (type %d has %d of %d)", stack, layer, t, gs.nchild, need);
+    first = 0;
+    last = gs.nchild;
+  }
+  const GroupShape &gs = lo.gs[t][g];
+  const int tkey = is_mlp_group(g) ? 0 : t;
+  const int64_t w0off = lo.w0_at(b, tkey, g);
+  const LayerOff &lf = lo.lay[layer];
+  uint8_t *A = h->arena;
+  wl::CallDesc &c = rv.c;
+  std::memset(&c, 0, sizeof c);
+  const int rs0 = gs.row_start[first];
+  const int z0 = gs.zoff[first];
+  c.K = gs.K;
+  c.W0 = reinterpret_cast<const uint16_t *>(A + w0off) + static_cast<size_t>(rs0) * gs.K;
+  c.s = reinterpret_cast<const float *>(A + lf.s[g]) + rs0;
+  c.Vt = reinterpret_cast<const uint16_t *>(A + lf.vt[g]) + static_cast<size_t>(z0) * gs.K;
+  c.nchild = last - first;
+  int ycol = 0;
+  c.Ntot = 0;
+  c.Rz = 0;
+  for (int i = first; i < last; ++i) {
+    wl::ChildDesc &ch = c.ch[i - first];
+    ch.U = reinterpret_cast<const uint16_t *>(A + lf.u[g][i]);
+    ch.row_start = gs.row_start[i] - rs0;
+    ch.N = gs.N[i];
+    ch.rpad = gs.rpad[i];
+    ch.zoff = gs.zoff[i] - z0;
+    ch.y_off = ycol;
+    ycol += gs.N[i];
+    ch.dup_off = -1;
+    c.Ntot += gs.N[i];
+    c.Rz += gs.rpad[i];
+  }
+  if (!single && gs.tied) {
+    // q | k | k: the k child also writes the v slot right after itself.
+    wl::ChildDesc &kch = c.ch[gs.child_of_fam[WL_K]];
+    kch.dup_off = ycol;
+    ycol += kch.N;
+  }
+  rv.out_dim = ycol;
+  return WL_OK;
+}
+
+wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t stack, const void *d_x,
+                   int32_t T, void *d_y, void *d_ws, size_t ws_bytes, void *stream) {
+  Resolved rv;
+  wl_status st = resolve(h, layer, family, stack, rv);
+  if (st != WL_OK) return st;
+  if (T < 0) return fail(WL_EINVAL, "T = %d is negative", T);
+  if (T > kMaxDim) return fail(WL_ESHAPE, "T = %d too large", T);
+  if (T == 0) return WL_OK;
+  if (!d_x || !d_y || !d_ws) return fail(WL_EINVAL, "x, y and workspace must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(d_x) % 16) return fail(WL_EINVAL, "x must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(d_y) % 2) return fail(WL_EINVAL, "y must be 2-byte aligned");
+  if (reinterpret_cast<uintptr_t>(d_ws) % 256) return fail(WL_EINVAL, "workspace must be 256-byte aligned");
+  const size_t need = ws_bytes_for(h->lo, T);
+  if (ws_bytes < need) return fail(WL_ENOSPACE, "workspace has %zu bytes, call needs %zu", ws_bytes, need);
+  const uint8_t *xb = static_cast<const uint8_t *>(d_x);
+  const uint8_t *yb = static_cast<const uint8_t *>(d_y);
+  const size_t xbytes = static_cast<size_t>(T) * rv.c.K * 2, ybytes = static_cast<size_t>(T) * rv.out_dim * 2;
+  if (xb < yb + ybytes && yb < xb + xbytes) return fail(WL_EINVAL, "y must not overlap x");
+  rv.c.x = static_cast<const uint16_t *>(d_x);
+  rv.c.y = static_cast<uint16_t *>(d_y);
+  rv.c.T = T;
+  rv.c.ldy = rv.out_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *ws = static_cast<uint8_t *>(d_ws);
+  const size_t zb = align256(static_cast<size_t>(wl::kDecodeMaxT) * h->lo.Rmax * 2);
+  hipError_t e;
+  if (T <= wl::kDecodeMaxT) {
+    wl::DecodeWs dw;
+    dw.ctrl = reinterpret_cast<uint32_t *>(ws);
+    dw.zhi = reinterpret_cast<uint16_t *>(ws + wl::kCtrlBytes);
+    dw.zlo = reinterpret_cast<uint16_t *>(ws + wl::kCtrlBytes + zb);
+    dw.ldz = h->lo.Rmax;
+    e = wl::launch_decode(rv.c, dw, s);
+  } else {
+    e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws + wl::kCtrlBytes + 2 * zb), s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return WL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *wl_last_error(void) { return g_err.c_str(); }
+
+size_t theta_bundle_arena_bytes(const wl_bundle_spec *spec) {
+  Layout lo;
+  if (make_layout(spec, lo) != WL_OK) return 0;
+  g_err.clear();
+  return lo.bytes;
+}
+
+wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size_t n_src, void *d_arena,
+                            size_t arena_bytes, void *stream, wl_bundle **out) {
+  if (!out) return fail(WL_EINVAL, "out is NULL");
+  *out = nullptr;
+  Layout lo;
+  wl_status st = make_layout(spec, lo);
+  if (st != WL_OK) return st;
+  if (!d_arena) return fail(WL_EINVAL, "arena is NULL");
+  if (reinterpret_cast<uintptr_t>(d_arena) % 256) return fail(WL_EINVAL, "arena must be 256-byte aligned");
+  if (arena_bytes < lo.bytes) return fail(WL_ENOSPACE, "arena has %zu bytes, bundle needs %zu", arena_bytes, lo.bytes);
+  if (n_src && !srcs) return fail(WL_EINVAL, "srcs is NULL");
+
+  // Expected sources.
+  using Key = std::array<int, 4>;  // kind, index, type key, family
+  std::map<Key, int> expect;       // -> index in srcs, or -1 while missing
+  for (int b = 0; b < lo.G; ++b)
+    for (int t = 0; t < lo.NT; ++t)
+      for (int g = 0; g < kGroups; ++g) {
+        if (lo.w0_at(b, t, g) < 0) continue;
+        const GroupShape &gs = lo.gs[t][g];
+        for (int c = 0; c < gs.nchild; ++c) expect[Key{WL_SRC_W0, b, t, gs.fam[c]}] = -1;
+      }
+  for (int l = 0; l < lo.L; ++l) {
+    const int t = lo.ltype[l];
+    for (int g = 0; g < kGroups; ++g) {
+      const GroupShape &gs = lo.gs[t][g];
+      for (int c = 0; c < gs.nchild; ++c) {
+        expect[Key{WL_SRC_S, l, 0, gs.fam[c]}] = -1;
+        if (gs.r[c] > 0) {
+          expect[Key{WL_SRC_U, l, 0, gs.fam[c]}] = -1;
+          expect[Key{WL_SRC_V, l, 0, gs.fam[c]}] = -1;
+        }
+      }
+    }
+  }
+  for (size_t i = 0; i < n_src; ++i) {
+    const wl_src &s = srcs[i];
+    if (s.kind < WL_SRC_W0 || s.kind > WL_SRC_V) return fail(WL_EINVAL, "source %zu: kind %d invalid", i, s.kind);
+    if (s.family < 0 || s.family >= WL_NUM_FAMILIES) return fail(WL_EINVAL, "source %zu: family %d invalid", i, s.family);
+    if (!s.ptr) return fail(WL_EINVAL, "source %zu: ptr is NULL", i);
+    const int want_dtype = s.kind == WL_SRC_S ? WL_DTYPE_F32 : WL_DTYPE_BF16;
+    if (s.dtype != want_dtype)
+      return fail(WL_EDTYPE, "source %zu (kind %d): dtype %d, required %d", i, s.kind, s.dtype, want_dtype);
+    int tkey = 0;
+    if (s.kind == WL_SRC_W0 && !is_mlp_family(s.family)) tkey = s.layer_type;
+    const Key k{s.kind, s.index, tkey, s.family};
+    auto it = expect.find(k);
+    if (it == expect.end())
+      return fail(WL_EINVAL, "source %zu (kind %d, index %d, type %d, family %d) is not part of this bundle", i, s.kind,
+                  s.index, s.layer_type, s.family);
+    if (it->second >= 0) return fail(WL_EINVAL, "source %zu duplicates source %d", i, it->second);
+    it->second = static_cast<int>(i);
+  }
+  for (const auto &kv : expect)
+    if (kv.second < 0)
+      return fail(WL_EINVAL, "missing source: kind %d, index %d, type %d, family %d", kv.first[0], kv.first[1],
+                  kv.first[2], kv.first[3]);
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  uint8_t *A = static_cast<uint8_t *>(d_arena);
+  hipError_t e = wl::launch_fill_zero(A, lo.bytes, strm);
+  if (e != hipSuccess) return hip_fail(e, "arena fill");
+  std::vector<std::vector<uint16_t>> host_tmp;
+  bool any_host = false;
+  for (const auto &kv : expect) {
+    const wl_src &s = srcs[kv.second];
+    const hipMemcpyKind kind = s.on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+    any_host |= !s.on_device;
+    if (s.kind == WL_SRC_W0) {
+      const int t = kv.first[2];
+      const int g = kGroupOf[s.family];
+      const GroupShape &gs = lo.gs[t][g];
+      const int c = gs.child_of_fam[s.family];
+      uint8_t *dst = A + lo.w0_at(s.index, t, g) + static_cast<size_t>(gs.row_start[c]) * gs.K * 2;
+      e = hipMemcpyAsync(dst, s.ptr, static_cast<size_t>(gs.N[c]) * gs.K * 2, kind, strm);
+      if (e != hipSuccess) return hip_fail(e, "W0 copy");
+      continue;
+    }
+    const int l = s.index;
+    const int t = lo.ltype[l];
+    const int g = kGroupOf[s.family];
+    const GroupShape &gs = lo.gs[t][g];
+    const int c = gs.child_of_fam[s.family];
+    const LayerOff &lf = lo.lay[l];
+    const int N = gs.N[c], K = gs.K, r = gs.r[c];
+    if (s.kind == WL_SRC_S) {
+      e = hipMemcpyAsync(A + lf.s[g] + static_cast<size_t>(gs.row_start[c]) * 4, s.ptr, static_cast<size_t>(N) * 4, kind, strm);
+    } else if (s.kind == WL_SRC_U) {
+      uint8_t *dst = A + lf.u[g][c];
+      if (r == gs.rpad[c])
+        e = hipMemcpyAsync(dst, s.ptr, static_cast<size_t>(N) * r * 2, kind, strm);
+      else
+        e = hipMemcpy2DAsync(dst, static_cast<size_t>(gs.rpad[c]) * 2, s.ptr, static_cast<size_t>(r) * 2,
+                             static_cast<size_t>(r) * 2, N, kind, strm);
+    } else {  // V [K, r] -> V^T rows zoff.. of the group block
+      uint16_t *dst = reinterpret_cast<uint16_t *>(A + lf.vt[g]) + static_cast<size_t>(gs.zoff[c]) * K;
+      if (s.on_device) {
+        e = wl::launch_transpose_v(static_cast<const uint16_t *>(s.ptr), K, r, dst, strm);
+      } else {
+        const uint16_t *V = static_cast<const uint16_t *>(s.ptr);
+        host_tmp.emplace_back(static_cast<size_t>(r) * K);
+        std::vector<uint16_t> &vt = host_tmp.back();
+        for (int k = 0; k < K; ++k)
+          for (int j = 0; j < r; ++j) vt[static_cast<size_t>(j) * K + k] = V[static_cast<size_t>(k) * r + j];
+        e = hipMemcpyAsync(dst, vt.data(), vt.size() * 2, hipMemcpyHostToDevice, strm);
+      }
+    }
+    if (e != hipSuccess) return hip_fail(e, "bundle copy");
+  }
+  if (any_host) {
+    e = hipStreamSynchronize(strm);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize after host copies");
+  }
+  wl_bundle *h = new wl_bundle;
+  h->lo = std::move(lo);
+  h->arena = A;
+  h->arena_bytes = arena_bytes;
+  *out = h;
+  g_err.clear();
+  return WL_OK;
+}
+
+wl_status theta_bundle_free(wl_bundle *bundle) {
+  delete bundle;
+  return WL_OK;
+}
+
+size_t weightless_workspace_bytes(const wl_bundle *bundle, int32_t T) {
+  if (!bundle) {
+    fail(WL_EINVAL, "bundle is NULL");
+    return 0;
+  }
+  if (T < 0) {
+    fail(WL_EINVAL, "T = %d is negative", T);
+    return 0;
+  }
+  return ws_bytes_for(bundle->lo, T);
+}
+
+wl_status weightless_workspace_init(void *d_ws, size_t ws_bytes, void *stream) {
+  if (!d_ws) return fail(WL_EINVAL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(d_ws) % 256) return fail(WL_EINVAL, "workspace must be 256-byte aligned");
+  if (ws_bytes < wl::kCtrlBytes) return fail(WL_ENOSPACE, "workspace smaller than %zu bytes", wl::kCtrlBytes);
+  hipError_t e = wl::launch_fill_zero(d_ws, ws_bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "workspace fill");
+  return WL_OK;
+}
+
+wl_status weightless_workspace_error(const void *d_ws, void *stream, uint32_t *out) {
+  if (!d_ws || !out) return fail(WL_EINVAL, "workspace and out must be non-NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(out, static_cast<const uint32_t *>(d_ws) + wl::kCtrlError, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "workspace error read");
+  return WL_OK;
+}
+
+wl_status weightless_linear(const wl_bundle *bundle, int32_t layer, int32_t family, const void *d_x, int32_t T,
+                            void *d_y, void *d_ws, size_t ws_bytes, void *stream) {
+  return run_call(bundle, layer, family, -1, d_x, T, d_y, d_ws, ws_bytes, stream);
+}
+
+wl_status weightless_stacked_linear(const wl_bundle *bundle, int32_t layer, int32_t stack, const void *d_x, int32_t T,
+                                    void *d_y, void *d_ws, size_t ws_bytes, void *stream) {
+  if (stack < 0) return fail(WL_ERANGE, "stack %d out of range", stack);
+  return run_call(bundle, layer, -1, stack, d_x, T, d_y, d_ws, ws_bytes, stream);
+}
+
+int32_t weightless_out_dim(const wl_bundle *bundle, int32_t layer, int32_t family, int32_t stack) {
+  Resolved rv;
+  if (resolve(bundle, layer, stack >= 0 ? -1 : family, stack >= 0 ? stack : -1, rv) != WL_OK) return 0;
+  return rv.out_dim;
+}
+
+}  // extern "C"
