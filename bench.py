@@ -1,0 +1,332 @@
+"""Benchmark of the weightless linear on one MI355X.
+
+A decode step is one pass of every layer's linears of the Gemma-4-31B-shaped
+sliding-attention workload at T=1 (60 layers x [stacked q|k|v, o, stacked
+gate|up, down], G=5 bands, rank 256), replayed from a captured HIP graph with
+the bundle and activations resident in HBM.  value = algorithmic bytes read
+per step (W0 + s + U + V^T + x of every call) / step time.
+
+The same run also times
+  * the same step at T=16,
+  * the Gemma-3-1B-shaped decode step (G=13, r=32, T=1),
+  * prefill steps (MFMA path): Gemma-4-31B mixed attention (10 full + 50
+    sliding layers, G=1 per type, r=1024, T=512) and Gemma-3-1B (G=1, r=64,
+    T=2048, 7 single-family calls per layer), in TFLOP/s,
+  * per-launch kernel durations with HIP events on the launch stream (the
+    roofline figure), and
+  * the fp64 CPU oracle on a bounded sample of the headline workload.
+
+Prints one JSON line.  Runs on one GPU only.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+CALLS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def call_bytes(wl, layer, fams, T):
+    """Algorithmic bytes a call must read: 2NK (W0) + 4N (s) + 2Nr (U) +
+    2Kr (V^T) per child, plus 2TK (x) once; and the bytes it writes (2TN)."""
+    lt = wl.layer_types[layer]
+    rd = 0
+    wr = 0
+    K = None
+    for f in fams:
+        N, K = wl.shape(lt, f)
+        if not wl.has(lt, f):        # tied v: output copy, no bundle read
+            wr += 2 * T * N
+            continue
+        r = wl.clamped_rank(lt, f)
+        rd += 2 * N * K + 4 * N + 2 * N * r + 2 * K * r
+        wr += 2 * T * N
+    return rd + 2 * T * K, wr
+
+
+def call_flops(wl, layer, fams, T):
+    lt = wl.layer_types[layer]
+    fl = 0
+    for f in fams:
+        if not wl.has(lt, f):
+            continue
+        N, K = wl.shape(lt, f)
+        r = wl.clamped_rank(lt, f)
+        fl += 2 * T * N * K + 2 * T * K * r + 2 * T * N * r
+    return fl
+
+
+class Step:
+    """Every call of every layer, with preallocated inputs and outputs."""
+
+    def __init__(self, wl, bundle, T, calls, dev):
+        import torch
+        self.items = []
+        self.bytes_rd = 0
+        self.bytes_wr = 0
+        self.flops = 0
+        self.per_call = {}
+        for layer in range(wl.num_layers):
+            for name, fams in calls:
+                lt = wl.layer_types[layer]
+                fams_here = [f for f in fams if (lt, f) in wl.dims or (f == "v" and lt in wl.k_eq_v_types)]
+                x = wl.x(layer, name, T, dev)
+                stacked = len(fams) > 1
+                width = bundle.out_dim(layer, stack=name) if stacked else bundle.out_dim(layer, family=name)
+                y = torch.empty((T, width), dtype=torch.bfloat16, device=dev)
+                rd, wr = call_bytes(wl, layer, fams_here, T)
+                fl = call_flops(wl, layer, fams_here, T)
+                self.items.append((layer, name, stacked, x, y))
+                self.bytes_rd += rd
+                self.bytes_wr += wr
+                self.flops += fl
+                pc = self.per_call.setdefault(name, {"calls": 0, "bytes": 0, "flops": 0})
+                pc["calls"] += 1
+                pc["bytes"] += rd
+                pc["flops"] += fl
+        self.bundle = bundle
+        self.ws = bundle.workspace(T)
+
+    def run(self):
+        b, ws = self.bundle, self.ws
+        for layer, name, stacked, x, y in self.items:
+            if stacked:
+                b.stacked(layer, name, x, y=y, ws=ws)
+            else:
+                b.linear(layer, name, x, y=y, ws=ws)
+
+
+def time_graph(step, steps, warmup):
+    """Capture the step in a HIP graph; time `steps` replays after `warmup`."""
+    import torch
+    step.run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step.run()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps, g
+
+
+def time_launches(step, reps):
+    """Per-call-type average duration with HIP events recorded on the launch
+    stream around each call, in step order (so W0 re-reads across layers see
+    the same cache state as in the step)."""
+    import torch
+    names = list(step.per_call)
+    evs = []
+    for _ in range(reps):
+        for layer, name, stacked, x, y in step.items:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if stacked:
+                step.bundle.stacked(layer, name, x, y=y, ws=step.ws)
+            else:
+                step.bundle.linear(layer, name, x, y=y, ws=step.ws)
+            e1.record()
+            evs.append((name, e0, e1))
+    torch.cuda.synchronize()
+    tot = {n: 0.0 for n in names}
+    cnt = {n: 0 for n in names}
+    for name, e0, e1 in evs:
+        tot[name] += e0.elapsed_time(e1) * 1e-3
+        cnt[name] += 1
+    return {n: tot[n] / cnt[n] for n in names}
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "weight_shared_rank_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file, sha, launches_per_unit):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    rec = d.get(kernel_file)
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def decode_section(wl, T, steps, warmup, dev, reps=3):
+    import synth.device as sdev
+    import torch
+    log(f"load {wl.name}")
+    bundle = sdev.load(wl, dev)
+    torch.cuda.synchronize()
+    step = Step(wl, bundle, T, CALLS, dev)
+    t_step, g = time_graph(step, steps, warmup)
+    durs = time_launches(step, reps)
+    launches = sum(pc["calls"] for pc in step.per_call.values())
+    per_call = {}
+    for n, pc in step.per_call.items():
+        b_per = pc["bytes"] / pc["calls"]
+        per_call[n] = {"bytes": b_per, "us": durs[n] * 1e6, "GBps": b_per / durs[n] / 1e9,
+                       "hbm_frac": b_per / durs[n] / 1e9 / HBM_PEAK_GBS}
+    kern_time = sum(durs[n] * pc["calls"] for n, pc in step.per_call.items())
+    out = {"step_s": t_step, "bytes_read": step.bytes_rd, "bytes_written": step.bytes_wr,
+           "GBps": step.bytes_rd / t_step / 1e9, "launches": launches,
+           "kernel_GBps": step.bytes_rd / kern_time / 1e9,
+           "avg_launch_us": kern_time / launches * 1e6, "bytes_per_launch": step.bytes_rd / launches,
+           "per_call": per_call}
+    del g, step, bundle
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def prefill_section(wl, T, calls, steps, warmup, dev, reps=1):
+    import synth.device as sdev
+    import torch
+    log(f"load {wl.name}")
+    bundle = sdev.load(wl, dev)
+    torch.cuda.synchronize()
+    step = Step(wl, bundle, T, calls, dev)
+    t_step, g = time_graph(step, steps, warmup)
+    durs = time_launches(step, reps)
+    launches = sum(pc["calls"] for pc in step.per_call.values())
+    per_call = {n: {"flops": pc["flops"] / pc["calls"], "us": durs[n] * 1e6,
+                    "TFLOPs": pc["flops"] / pc["calls"] / durs[n] / 1e12} for n, pc in step.per_call.items()}
+    kern_time = sum(durs[n] * pc["calls"] for n, pc in step.per_call.items())
+    out = {"step_s": t_step, "flops": step.flops, "TFLOPs": step.flops / t_step / 1e12,
+           "mfma_frac": step.flops / t_step / 1e12 / BF16_PEAK_TFLOPS,
+           "call_TFLOPs": step.flops / kern_time / 1e12, "calls": launches, "per_call": per_call}
+    del g, step, bundle
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(wl, T, budget_s, dev):
+    """The fp64 oracle (as it stands) on one layer's four calls of the
+    headline workload, repeated until about budget_s of CPU time."""
+    import numpy as np
+    from oracle import forward
+    from oracle.workload import OracleWorkload
+    ow = OracleWorkload(wl, dev, cache_w0=8)
+    layer = 0
+    prepared = []
+    nbytes = 0
+    for name, fams in CALLS:
+        x = wl.x(layer, name, T, dev).float().cpu().double().numpy()
+        children = [ow.params(layer, f) for f in fams]
+        prepared.append((x, children))
+        nbytes += call_bytes(wl, layer, fams, T)[0]
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((i.get("num_threads", 1) for i in info), default=1)
+    except Exception:
+        cores = os.cpu_count()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for x, children in prepared:
+            forward.stacked(x, children)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 5000:
+            break
+    return {"value": nbytes * n / el / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle, layer 0 of the headline workload (4 calls, {nbytes/1e9:.3f} GB of "
+                      f"bundle bytes), repeated {n}x in {el:.1f} s; W0/s/U/V pre-upcast to fp64 outside the timing"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--only", default="all", choices=["all", "decode", "prefill"])
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the weightless linear here runs on a single MI355X "
+              "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    from weight_shared_rank_amd import binding
+    binding.lib()
+
+    res = {}
+    wl4 = synth.workload(4)
+    if args.only in ("all", "decode"):
+        res["decode4_t1"] = decode_section(wl4, 1, args.steps, args.warmup, dev)
+        log(f"decode T=1: {res['decode4_t1']['GBps']:.1f} GB/s")
+        res["decode4_t16"] = decode_section(wl4, 16, args.steps, args.warmup, dev)
+        log(f"decode T=16: {res['decode4_t16']['GBps']:.1f} GB/s")
+        res["decode2_t1"] = decode_section(synth.custom(26, 13, 32, dict(synth.workload(2).dims), cid=2),
+                                           1, args.steps * 5, args.warmup, dev)
+        log(f"gemma3 decode T=1: {res['decode2_t1']['GBps']:.1f} GB/s")
+    if args.only in ("all", "prefill"):
+        res["prefill5"] = prefill_section(synth.workload(5), 512, CALLS, max(2, args.steps // 4), 2, dev)
+        log(f"prefill w5: {res['prefill5']['TFLOPs']:.1f} TFLOP/s")
+        singles = tuple((f, (f,)) for f in synth.FAMILIES)
+        res["prefill3"] = prefill_section(synth.workload(3), 2048, singles, args.steps, args.warmup, dev)
+        log(f"prefill w3: {res['prefill3']['TFLOPs']:.1f} TFLOP/s")
+
+    line = {"metric": "weightless-linear decode GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded normal bundles and activations of the stated shapes)"}
+    if "decode4_t1" in res:
+        d = res["decode4_t1"]
+        line.update({"value": round(d["GBps"], 2), "ms_per_step": round(d["step_s"] * 1e3, 4),
+                     "config": {"workload": "gemma4-31b-sliding decode: 60 layers x (qkv stacked, o, gate_up "
+                                            "stacked, down), G=5, rank 256, T=1, graph-replayed step",
+                                "tokens": 1, "layers": 60, "bands": 5, "rank": 256,
+                                "bytes_read_per_step": d["bytes_read"], "hbm_frac": d["GBps"] / HBM_PEAK_GBS}})
+        sha = source_sha("decode.hip", "common.h", "internal.h")
+        line["roofline"] = {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(d["kernel_GBps"], 2),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(d["kernel_GBps"] / HBM_PEAK_GBS, 4),
+                            "bytes_per_launch": d["bytes_per_launch"], "avg_launch_us": round(d["avg_launch_us"], 3),
+                            "traffic": traffic_from_profile("decode.hip", sha, 1), "source_sha": sha}
+    line["detail"] = res
+    if "prefill5" in res:
+        p = res["prefill5"]
+        line["prefill"] = {"metric": "prefill TFLOP/s", "value": round(p["TFLOPs"], 2), "unit": "TFLOP/s",
+                           "mfma_frac": round(p["mfma_frac"], 4), "peak": BF16_PEAK_TFLOPS,
+                           "workload": "gemma4-31b mixed prefill: 10 full + 50 sliding layers, G=1 per type, "
+                                       "rank 1024, T=512, graph-replayed step"}
+    if not args.no_cpu and args.only in ("all", "decode"):
+        log("cpu baseline")
+        line["cpu_baseline"] = cpu_baseline(wl4, 1, args.cpu_budget, dev)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -132,34 +132,27 @@ wl_status theta_bundle_free(wl_bundle *bundle);
 
 /* Workspace bytes needed by any weightless_linear / weightless_stacked_linear
  * call on this bundle with T tokens (T <= 16: decode path; T > 16: prefill
- * path).  0 with wl_last_error() set on error. */
+ * path).  The workspace holds intermediate results of one call (the K-slice
+ * partials of V^T x for decode, Z = X V for prefill); it needs no
+ * initialization and keeps nothing between calls.  0 with wl_last_error()
+ * set on error. */
 size_t weightless_workspace_bytes(const wl_bundle *bundle, int32_t T);
-
-/* Prepare a workspace for first use: enqueues a fill of d_ws with zeros on
- * `stream` (a kernel, not a memset node).  Calls leave the workspace's
- * synchronization words at zero when they finish, so this is needed once per
- * workspace, not per call. */
-wl_status weightless_workspace_init(void *d_ws, size_t ws_bytes, void *stream);
-
-/* Copy the workspace's sticky error word to *out (0 = no device-side error;
- * bit 0 = a decode launch gave up waiting for its V^T x reduction).
- * This call synchronizes `stream`. */
-wl_status weightless_workspace_error(const void *d_ws, void *stream, uint32_t *out);
 
 /* y = s (.) (W0 x) + U (V^T x) for one family of one layer.
  *  d_x bf16 [T, K], d_y bf16 [T, N] (must not alias d_x), T >= 0 (T = 0: no-op).
- *  T <= 16 runs the decode kernel (one launch), T > 16 the prefill MFMA GEMMs
- *  (two launches: Z = X V, then Y = (X W0^T) (.) s + Z U^T).
+ *  T <= 16 runs the decode path (two launches: the K-slice partials of
+ *  z = V^T x, then the W0 stream with the fused scale and U z epilogue),
+ *  T > 16 the prefill MFMA GEMMs (two launches: Z = X V, then
+ *  Y = (X W0^T) (.) s + Z U^T).
  *  family WL_V on a K=V-tied layer type evaluates k's bundle.
  *  d_ws: workspace of at least weightless_workspace_bytes(bundle, T) bytes,
- *  initialized once with weightless_workspace_init; concurrent calls need
- *  distinct workspaces. */
+ *  256-byte aligned; concurrent calls need distinct workspaces. */
 wl_status weightless_linear(const wl_bundle *bundle, int32_t layer, int32_t family,
                             const void *d_x, int32_t T, void *d_y,
                             void *d_ws, size_t ws_bytes, void *stream);
 
-/* The stacked call: q|k|v (or gate|up) of one layer over one x in a single
- * decode launch (two for prefill).  d_y bf16 [T, N_q + N_k + N_v] (resp.
+/* The stacked call: q|k|v (or gate|up) of one layer over one x: the same
+ * launches as a single-family call, over all children's rows at once.  d_y bf16 [T, N_q + N_k + N_v] (resp.
  * [T, N_gate + N_up]).  On a K=V-tied layer type the v slot receives a copy of
  * k's output, so the output layout is the same on every layer. */
 wl_status weightless_stacked_linear(const wl_bundle *bundle, int32_t layer, int32_t stack,

@@ -199,8 +199,4 @@ def test_empty_bundle_and_call_errors(L):
         assert L.theta_bundle_free(h) == 0
     assert L.theta_bundle_free(None) == 0
     assert L.weightless_linear(None, 0, 0, FAKE_ARENA, 1, FAKE_ARENA, FAKE_ARENA, 1, None) == -1
-    assert L.weightless_workspace_init(None, 1024, None) == -1
-    assert L.weightless_workspace_init(FAKE_ARENA + 8, 1024, None) == -1
-    assert L.weightless_workspace_init(FAKE_ARENA, 16, None) == -5
-    out = ctypes.c_uint32()
-    assert L.weightless_workspace_error(None, None, ctypes.byref(out)) == -1
+    assert L.weightless_workspace_bytes(None, 1) == 0

@@ -131,9 +131,8 @@ def test_host_sources_match_device_sources(gpu_lib):
 
 
 def test_graph_replay(gpu_lib):
-    """Decode launches leave their synchronization words at zero, so a captured
-    graph replays correctly; checked on several replays with eager work and
-    synchronizations in between."""
+    """A captured graph of decode and prefill calls replays correctly; checked
+    on several replays with eager work and synchronizations in between."""
     wl = ragged(9)
     b = sdev.load(wl, DEV)
     xs = wl.x(1, "qkv", 3, DEV)
@@ -160,4 +159,3 @@ def test_graph_replay(gpu_lib):
         assert torch.equal(ys, ref_s) and torch.equal(yp, ref_p), f"replay {rep}"
         b.stacked(1, "qkv", xs)       # eager work between replays
         torch.cuda.synchronize()
-    assert b.workspace_error(ws_d) == 0

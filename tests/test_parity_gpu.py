@@ -90,7 +90,6 @@ def test_workload1_token_sweep(w1, T):
     y = b.linear(1, "up", x)
     torch.cuda.synchronize()
     check(y, ow.call(1, "up", np64(x)), f"w1 T={T}")
-    assert b.workspace_error(b._ws_for(T, None)) == 0
 
 
 # --------------------------------------------------------------------------

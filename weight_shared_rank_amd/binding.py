@@ -27,7 +27,7 @@ DECODE_MAX_T = 16
 
 # every symbol include/weightless.h declares
 EXPORTS = ("theta_bundle_arena_bytes", "theta_bundle_load", "theta_bundle_free",
-           "weightless_workspace_bytes", "weightless_workspace_init", "weightless_workspace_error",
+           "weightless_workspace_bytes",
            "weightless_linear", "weightless_stacked_linear", "weightless_out_dim", "wl_last_error")
 
 
@@ -68,8 +68,6 @@ def lib():
                                     ctypes.POINTER(vp)]),
         "theta_bundle_free": (i32, [vp]),
         "weightless_workspace_bytes": (sz, [vp, i32]),
-        "weightless_workspace_init": (i32, [vp, sz, vp]),
-        "weightless_workspace_error": (i32, [vp, vp, ctypes.POINTER(ctypes.c_uint32)]),
         "weightless_linear": (i32, [vp, i32, i32, vp, i32, vp, vp, sz, vp]),
         "weightless_stacked_linear": (i32, [vp, i32, i32, vp, i32, vp, vp, sz, vp]),
         "weightless_out_dim": (i32, [vp, i32, i32, i32]),
@@ -188,12 +186,9 @@ class ThetaBundle:
         return n
 
     def workspace(self, T: int, stream=None):
-        """A zero-initialized workspace large enough for T tokens."""
+        """A workspace large enough for T tokens."""
         import torch
-        n = self.workspace_bytes(T)
-        ws = torch.empty(n, dtype=torch.uint8, device=self.arena.device)
-        _check(lib().weightless_workspace_init(ws.data_ptr(), n, _stream_ptr(stream)))
-        return ws
+        return torch.empty(self.workspace_bytes(T), dtype=torch.uint8, device=self.arena.device)
 
     def _ws_for(self, T, stream):
         need = self.workspace_bytes(T)
@@ -203,11 +198,6 @@ class ThetaBundle:
             ws = self.workspace(T, stream)
             self._ws[key] = ws
         return ws
-
-    def workspace_error(self, ws, stream=None) -> int:
-        out = ctypes.c_uint32()
-        _check(lib().weightless_workspace_error(ws.data_ptr(), _stream_ptr(stream), ctypes.byref(out)))
-        return out.value
 
     def _call(self, fn, layer, code, x, y, ws, stream, width):
         import torch

@@ -11,10 +11,9 @@ namespace wl {
 constexpr int kDecodeMaxT = 16;
 constexpr int kMaxChildren = 3;
 
-// Workspace header words (uint32 each, at the start of the workspace).
-enum CtrlWord { kCtrlError = 0, kCtrlZReady = 1, kCtrlDone = 2 };
-constexpr size_t kCtrlBytes = 256;
-constexpr uint32_t kErrZWaitTimeout = 1u;
+// Decode path: z = V^T x is computed in at most kDecodeMaxSlices K slices;
+// the workspace holds their fp32 partials [slice][16 tokens][Rz].
+constexpr int kDecodeMaxSlices = 16;
 
 // One child projection of a (possibly stacked) call, as the kernels see it.
 struct ChildDesc {
@@ -39,15 +38,10 @@ struct CallDesc {
   ChildDesc ch[kMaxChildren];
 };
 
-// Decode-path kernel launch (T <= 16): one launch computes z = V^T x, the
-// shared-block product and the fused epilogue.
-struct DecodeWs {
-  uint32_t *ctrl;      // workspace header
-  uint16_t *zhi;       // [16, ldz] bf16: z rounded to bf16
-  uint16_t *zlo;       // [16, ldz] bf16: z - zhi rounded to bf16
-  int32_t ldz;
-};
-hipError_t launch_decode(const CallDesc &c, const DecodeWs &ws, hipStream_t stream);
+// Decode path (T <= 16): launch 1 writes the K-slice partials of z = V^T x
+// into zpart, launch 2 streams W0 and fuses the scale and U z epilogue.
+int decode_z_slices(int Rz, int K);
+hipError_t launch_decode(const CallDesc &c, float *zpart, hipStream_t stream);
 
 // Prefill path (T > 16): Z = X V into zbuf [T, Rz] bf16, then the main GEMM
 // with the scale and rank-r epilogue.

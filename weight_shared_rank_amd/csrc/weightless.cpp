@@ -213,11 +213,16 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
   return WL_OK;
 }
 
+// Workspace: decode z partials [kDecodeMaxSlices][16][Rmax] fp32, then (T > 16)
+// the prefill Z [T][Rmax] bf16.
+size_t ws_decode_bytes(const Layout &lo) {
+  return align256(static_cast<size_t>(wl::kDecodeMaxSlices) * wl::kDecodeMaxT * lo.Rmax * 4);
+}
+
 size_t ws_bytes_for(const Layout &lo, int32_t T) {
-  const size_t zb = align256(static_cast<size_t>(wl::kDecodeMaxT) * lo.Rmax * 2);
-  size_t n = wl::kCtrlBytes + 2 * zb;
+  size_t n = ws_decode_bytes(lo);
   if (T > wl::kDecodeMaxT) n += align256(static_cast<size_t>(T) * lo.Rmax * 2);
-  return n;
+  return n < 256 ? 256 : n;
 }
 
 }  // namespace
@@ -328,18 +333,11 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
   rv.c.ldy = rv.out_dim;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *ws = static_cast<uint8_t *>(d_ws);
-  const size_t zb = align256(static_cast<size_t>(wl::kDecodeMaxT) * h->lo.Rmax * 2);
   hipError_t e;
-  if (T <= wl::kDecodeMaxT) {
-    wl::DecodeWs dw;
-    dw.ctrl = reinterpret_cast<uint32_t *>(ws);
-    dw.zhi = reinterpret_cast<uint16_t *>(ws + wl::kCtrlBytes);
-    dw.zlo = reinterpret_cast<uint16_t *>(ws + wl::kCtrlBytes + zb);
-    dw.ldz = h->lo.Rmax;
-    e = wl::launch_decode(rv.c, dw, s);
-  } else {
-    e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws + wl::kCtrlBytes + 2 * zb), s);
-  }
+  if (T <= wl::kDecodeMaxT)
+    e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), s);
+  else
+    e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws + ws_decode_bytes(h->lo)), s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return WL_OK;
 }
@@ -494,24 +492,6 @@ size_t weightless_workspace_bytes(const wl_bundle *bundle, int32_t T) {
     return 0;
   }
   return ws_bytes_for(bundle->lo, T);
-}
-
-wl_status weightless_workspace_init(void *d_ws, size_t ws_bytes, void *stream) {
-  if (!d_ws) return fail(WL_EINVAL, "workspace is NULL");
-  if (reinterpret_cast<uintptr_t>(d_ws) % 256) return fail(WL_EINVAL, "workspace must be 256-byte aligned");
-  if (ws_bytes < wl::kCtrlBytes) return fail(WL_ENOSPACE, "workspace smaller than %zu bytes", wl::kCtrlBytes);
-  hipError_t e = wl::launch_fill_zero(d_ws, ws_bytes, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "workspace fill");
-  return WL_OK;
-}
-
-wl_status weightless_workspace_error(const void *d_ws, void *stream, uint32_t *out) {
-  if (!d_ws || !out) return fail(WL_EINVAL, "workspace and out must be non-NULL");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(out, static_cast<const uint32_t *>(d_ws) + wl::kCtrlError, 4, hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return hip_fail(e, "workspace error read");
-  return WL_OK;
 }
 
 wl_status weightless_linear(const wl_bundle *bundle, int32_t layer, int32_t family, const void *d_x, int32_t T,
