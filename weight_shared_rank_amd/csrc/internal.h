@@ -11,9 +11,9 @@ namespace wl {
 constexpr int kDecodeMaxT = 16;
 constexpr int kMaxChildren = 3;
 
-// Decode path: z = V^T x is computed in at most kDecodeMaxSlices K slices;
-// the workspace holds their fp32 partials [slice][16 tokens][Rz].
-constexpr int kDecodeMaxSlices = 16;
+// Decode path: the stream launch splits K into at most kDecodeMaxSlices
+// slices and writes fp32 partials [slice][token][row] of W0 x and V^T x.
+constexpr int kDecodeMaxSlices = 8;
 
 // One child projection of a (possibly stacked) call, as the kernels see it.
 struct ChildDesc {
@@ -38,10 +38,11 @@ struct CallDesc {
   ChildDesc ch[kMaxChildren];
 };
 
-// Decode path (T <= 16): launch 1 writes the K-slice partials of z = V^T x
-// into zpart, launch 2 streams W0 and fuses the scale and U z epilogue.
-int decode_z_slices(int Rz, int K);
-hipError_t launch_decode(const CallDesc &c, float *zpart, hipStream_t stream);
+// Decode path (T <= 16): launch 1 streams [W0; V^T] x into the K-slice
+// partials p_part [KS][T][Ntot] and z_part [T][Rz] (V^T rows are not split);
+// launch 2 sums the partials and applies the scale and the U z epilogue.
+int decode_k_slices(int Ntot, int Rz, int K);
+hipError_t launch_decode(const CallDesc &c, float *p_part, float *z_part, hipStream_t stream);
 
 // Prefill path (T > 16): Z = X V into zbuf [T, Rz] bf16, then the main GEMM
 // with the scale and rank-r epilogue.

@@ -92,7 +92,8 @@ struct Layout {
   std::vector<int64_t> w0;  // [(band * NT + tkey) * kGroups + g], -1 if absent
   std::vector<LayerOff> lay;
   size_t bytes = 0;
-  int Rmax = 0;
+  int Rmax = 0;  // largest sum of padded ranks of a group
+  int Nmax = 0;  // largest sum of rows of a group
 
   int band(int l) const { return static_cast<int>((static_cast<int64_t>(l) * G) / L); }
   int64_t &w0_at(int b, int t, int g) { return w0[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
@@ -141,6 +142,7 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
   }
   // Group shapes per layer type.
   lo.Rmax = 0;
+  lo.Nmax = 0;
   for (int t = 0; t < NT; ++t) {
     for (int g = 0; g < kGroups; ++g) {
       GroupShape &gs = lo.gs[t][g];
@@ -171,6 +173,7 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
       }
       if (!gs.any) gs.tied = false;
       if (gs.Rtot > lo.Rmax) lo.Rmax = gs.Rtot;
+      if (gs.Ntot > lo.Nmax) lo.Nmax = gs.Ntot;
     }
   }
   // W0 regions: one per (band, type key, group) used by some layer.
@@ -213,15 +216,19 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
   return WL_OK;
 }
 
-// Workspace: decode z partials [kDecodeMaxSlices][16][Rmax] fp32, then (T > 16)
-// the prefill Z [T][Rmax] bf16.
-size_t ws_decode_bytes(const Layout &lo) {
-  return align256(static_cast<size_t>(wl::kDecodeMaxSlices) * wl::kDecodeMaxT * lo.Rmax * 4);
+// Workspace.  Decode (T <= 16): the stream launch's fp32 partials,
+// p_part [kDecodeMaxSlices][T][Nmax] then z_part [T][Rmax].
+// Prefill (T > 16): Z = X V as bf16 [T][Rmax].
+size_t ws_p_part_bytes(const Layout &lo, int32_t T) {
+  return align256(static_cast<size_t>(wl::kDecodeMaxSlices) * T * lo.Nmax * 4);
 }
 
 size_t ws_bytes_for(const Layout &lo, int32_t T) {
-  size_t n = ws_decode_bytes(lo);
-  if (T > wl::kDecodeMaxT) n += align256(static_cast<size_t>(T) * lo.Rmax * 2);
+  size_t n;
+  if (T <= wl::kDecodeMaxT)
+    n = ws_p_part_bytes(lo, T) + align256(static_cast<size_t>(T) * lo.Rmax * 4);
+  else
+    n = align256(static_cast<size_t>(T) * lo.Rmax * 2);
   return n < 256 ? 256 : n;
 }
 
@@ -335,9 +342,9 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
   uint8_t *ws = static_cast<uint8_t *>(d_ws);
   hipError_t e;
   if (T <= wl::kDecodeMaxT)
-    e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), s);
+    e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), reinterpret_cast<float *>(ws + ws_p_part_bytes(h->lo, T)), s);
   else
-    e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws + ws_decode_bytes(h->lo)), s);
+    e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws), s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return WL_OK;
 }
