@@ -114,7 +114,8 @@ typedef struct wl_bundle wl_bundle; /* opaque; host metadata only */
  * spec is invalid; wl_last_error() then says why).  The arena holds, 256-byte
  * aligned, each W0 once -- stacked groups [q;k;v] and [gate;up] with their
  * rows contiguous -- and per layer its s (float32), U (bf16, rows padded to a
- * multiple of 8 ranks) and V^T (bf16 [r, K], ranks padded to a multiple of 8). */
+ * multiple of 32 ranks) and V^T (bf16 [r, K], ranks padded to a multiple of
+ * 32), plus 256 zero bytes used by the kernels for masking. */
 size_t theta_bundle_arena_bytes(const wl_bundle_spec *spec);
 
 /* Pack a theta bundle into the caller's device arena (d_arena, 256-byte
@@ -132,10 +133,10 @@ wl_status theta_bundle_free(wl_bundle *bundle);
 
 /* Workspace bytes needed by any weightless_linear / weightless_stacked_linear
  * call on this bundle with T tokens (T <= 16: decode path; T > 16: prefill
- * path).  The workspace holds intermediate results of one call (the K-slice
- * partials of V^T x for decode, Z = X V for prefill); it needs no
- * initialization and keeps nothing between calls.  0 with wl_last_error()
- * set on error. */
+ * path).  The workspace holds intermediate results of one call (fp32 K-slice
+ * partials for decode, Z = X V for prefill); it needs no initialization and
+ * keeps nothing between calls.
+ * 0 with wl_last_error() set on error. */
 size_t weightless_workspace_bytes(const wl_bundle *bundle, int32_t T);
 
 /* y = s (.) (W0 x) + U (V^T x) for one family of one layer.

@@ -159,3 +159,32 @@ def test_graph_replay(gpu_lib):
         assert torch.equal(ys, ref_s) and torch.equal(yp, ref_p), f"replay {rep}"
         b.stacked(1, "qkv", xs)       # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_call_validation(gpu_lib):
+    """Argument errors of loaded-bundle calls return before any launch."""
+    import ctypes
+    L = binding.lib()
+    wl = ragged(5)
+    b = sdev.load(wl, DEV)
+    x = wl.x(0, "qkv", 4, DEV)
+    y = torch.empty((4, 1000), dtype=torch.bfloat16, device=DEV)
+    ws = b.workspace(4)
+    h = b.handle
+    args = lambda xp=x.data_ptr(), yp=y.data_ptr(), T=4, wsb=ws.numel(): (xp, T, yp, ws.data_ptr(), wsb, None)
+    assert L.weightless_linear(h, 3, 0, *args()) == -4            # layer out of range
+    assert "layer" in binding.last_error()
+    assert L.weightless_linear(h, -1, 0, *args()) == -4
+    assert L.weightless_linear(h, 0, 7, *args()) == -4            # family out of range
+    assert L.weightless_stacked_linear(h, 0, 2, *args()) == -4    # stack out of range
+    assert L.weightless_linear(h, 0, 0, *args(T=-1)) == -1        # negative T
+    assert L.weightless_linear(h, 0, 0, *args(xp=0)) == -1        # NULL x
+    assert L.weightless_linear(h, 0, 0, *args(xp=x.data_ptr() + 2)) == -1   # x not 16-byte aligned
+    assert L.weightless_linear(h, 0, 0, *args(wsb=16)) == -5      # workspace too small
+    assert L.weightless_linear(h, 0, 0, *args(T=0)) == 0          # T = 0 is a no-op
+    assert L.weightless_out_dim(h, 0, -1, 0) == 200 + 72 + 72
+    assert L.weightless_out_dim(h, 0, 0, -1) == 200
+    wl0 = synth.custom(2, 1, 4, {(0, "q"): (64, 64), (0, "k"): (32, 64)})
+    b0 = sdev.load(wl0, DEV)
+    assert L.weightless_stacked_linear(b0.handle, 0, 0, *args()) == -4      # v absent, not tied
+    assert L.weightless_linear(b0.handle, 0, 5, *args()) == -4              # up absent

@@ -20,7 +20,7 @@ struct ChildDesc {
   const uint16_t *U;   // [N, rpad] bf16, row-major (padded ranks are zero)
   int32_t row_start;   // first row of this child among the call's rows
   int32_t N;           // rows of this child
-  int32_t rpad;        // rank rounded up to a multiple of 8 (U row stride)
+  int32_t rpad;        // rank rounded up to a multiple of 32 (U row stride)
   int32_t zoff;        // first V^T row / z column of this child
   int32_t y_off;       // first output column of this child in y
   int32_t dup_off;     // second output column offset (K=V tying) or -1
@@ -44,9 +44,10 @@ struct CallDesc {
 int decode_k_slices(int Ntot, int Rz, int K);
 hipError_t launch_decode(const CallDesc &c, float *p_part, float *z_part, hipStream_t stream);
 
-// Prefill path (T > 16): Z = X V into zbuf [T, Rz] bf16, then the main GEMM
-// with the scale and rank-r epilogue.
-hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, hipStream_t stream);
+// Prefill path (T > 16): launch 1 computes Z = X V into zbuf [T][Rz] (bf16),
+// launch 2 the main GEMM with the scale and rank-r epilogue.  zero_row points
+// at >= 16 zero bytes (used to mask rows and k columns outside an operand).
+hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, const uint16_t *zero_row, hipStream_t stream);
 
 // Load-time helpers.
 hipError_t launch_fill_zero(void *dst, size_t bytes, hipStream_t stream);

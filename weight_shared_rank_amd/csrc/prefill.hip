@@ -1,25 +1,44 @@
-// Prefill-path kernels (T > 16 tokens): two bf16 MFMA GEMMs.
+// Prefill-path kernels (T > 16 tokens): two launches of one bf16 MFMA GEMM.
 //
-//   launch 1:  Z[T, Rz] = X[T, K] V          (bf16 out, the thin reduction)
-//   launch 2:  Y[T, N]  = (X W0^T) (.) s + Z U^T   (scale and rank-r delta
-//              fused into the epilogue of the shared-block GEMM; y is written
-//              once, in bf16)
+//   launch 1:  Z[T, Rz] = X[T, K] V              (the thin reduction, bf16 out)
+//   launch 2:  Y[T, N]  = (X W0^T) (.) s + Z U^T   (scale and rank-r delta fused
+//              into the epilogue of the shared-block GEMM; y written once)
 //
-// The forward is the method's theta-bundle forward ("Add a new model
-// architecture" page, introduction); the pages' GEMM formulation keeps bf16
-// operands with fp32 accumulation ("Quality (Gemma 4 31B)" page, "Kernel
-// optimizations > GEMM path"), as these kernels do.
+// The forward is the theta-bundle forward ("Add a new model architecture"
+// page, introduction); as in the pages' GEMM formulation the operands stay
+// bf16 with fp32 accumulation ("Quality (Gemma 4 31B)" page, "Kernel
+// optimizations > GEMM path").
 //
-// Both launches use one LDS-tiled kernel.  A workgroup owns a BM x BN tile of
-// the output: BM rows of the weight matrix (W0 or V^T: "features", the MFMA
-// A operand) by BN tokens (the B operand).  All operands are K-contiguous, so
-// every global load is a 16-byte row chunk and every LDS fragment read is one
-// 16-byte ds_read.  Tiles of A and B are staged through registers into a
-// double-buffered LDS ring (rows padded by 16 bytes against bank conflicts).
-// The epilogue of launch 2 scales the fp32 accumulators by s per feature row
-// and then runs the same staged loop over the ranks of each child (A = U
-// rows of that child, B = Z columns of that child), so the delta is computed
-// on the MFMA at the GEMM's own rate before y is rounded and stored.
+// GEMM core (gfx950).  A workgroup owns a BM x BN output tile: BM weight rows
+// ("features", MFMA A operand) by BN tokens (B operand).  Both operands are
+// K-contiguous rows.  Tiles of 32 k are moved global -> LDS by
+// global_load_lds_dwordx4 (no VGPR staging) into an NST-stage ring, so loads
+// run NST-1 k-tiles ahead of the MFMAs.  Each wave instruction fills 16
+// rows x 64 bytes (1 KB, lane i at byte 16 i); a lane fetches 16-byte chunk
+// c = (i % 4) ^ ((i / 8) % 4) of row i / 4.  This XOR-swizzles the LDS rows
+// (slot = chunk ^ ((row / 2) % 4)) so that each 8-lane phase of a 16-byte
+// fragment read (8 consecutive rows, one chunk) covers the 32 LDS banks
+// exactly once: no bank conflicts.  Lanes whose row or k lies outside the operand fetch a row of zeros
+// kept in the arena, which is how tails and foreign rows are masked (an LDS
+// DMA lane cannot be zero-filled).  Large tiles use eight waves (two per
+// SIMD, 64 x 128 or 64 x 64 each), small ones four.
+//
+// Scheduling.  Workgroups are numbered XCD-major: hardware assigns
+// workgroup w to XCD w % 8, and the tile order is remapped so that each XCD
+// walks a contiguous range of (feature tile, K slice, token tile), token tile
+// fastest: the token tiles that share a block of W0 run at the same time on
+// one XCD and read it from HBM once (later reads hit that XCD's L2).
+// Each launch takes the largest tile shape (256x256 down to 64x64) that
+// still gives every CU a workgroup.  K is never split across workgroups:
+// combining partial tiles across XCDs needs device-scope release/acquire,
+// which on this part writes back / invalidates a whole L2 and costs more than
+// the smaller tile.
+//
+// Epilogue of launch 2: the fp32 accumulators are scaled by s per feature
+// row, then the same staged loop runs over the ranks of every child whose
+// rows meet the tile (A = that child's U rows, other rows read the zero row;
+// B = the child's columns of Z), so U z is added at MFMA rate before y is
+// rounded to bf16 and stored.
 #include "common.h"
 #include "internal.h"
 
@@ -27,188 +46,312 @@ namespace wl {
 
 namespace {
 
-constexpr int BM = 128;   // features per workgroup
-constexpr int BN = 128;   // tokens per workgroup
-constexpr int BK = 64;    // k per stage
-constexpr int LDSW = BK + 8;  // padded LDS row, in bf16 elements (144 bytes)
-constexpr int NTHR = 256;
-// each thread stages BM*BK/8/NTHR = 4 vectors of A and 4 of B per stage
-constexpr int VPT_A = BM * BK / 8 / NTHR;
-constexpr int VPT_B = BN * BK / 8 / NTHR;
+typedef __attribute__((address_space(3))) void lds_void;
 
-struct Operand {
-  const uint16_t *ptr;  // element (row 0, col 0) of the operand matrix
-  int64_t ld;           // row stride in elements
-  int32_t row_lo, row_hi;  // valid rows [row_lo, row_hi) (others read as zero)
+constexpr int kNST = 4;       // LDS ring stages
+constexpr int kBK = 32;       // k per stage
+constexpr int kRowBytes = 64; // kBK bf16 per LDS row
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+struct GemmArgs {
+  // main segment: rows of A (weights) against rows of B (tokens), K long
+  const uint16_t *A;
+  int32_t M;
+  int64_t lda;
+  const uint16_t *B;
+  int32_t T;
+  int64_t ldb;
+  int32_t K;
+  const uint16_t *zero_row;  // >= 16 zero bytes
+  // tiling
+  int32_t nM, nT;     // feature tiles, token tiles
+  // epilogue
+  int32_t mode;       // 0: Y = bf16(acc) [T][ldy]; 1: scale + delta + child map
+  uint16_t *Y;
+  int32_t ldy;
+  const float *s;
+  const uint16_t *Z;  // [T][ldz] (mode 1)
+  int32_t ldz;
+  int32_t nchild;
+  ChildDesc ch[kMaxChildren];
 };
 
-// Stage one BK-wide slice [k0, k0 + BK) of `rows` rows starting at row0 into
-// registers; columns >= klen and rows outside [row_lo, row_hi) are zero.
-template <int ROWS, int VPT>
-__device__ __forceinline__ void stage_load(u32x4 (&v)[VPT], const Operand &op, int row0, int k0, int klen) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int idx = t + i * NTHR;
-    const int row = row0 + idx / (BK / 8);
-    const int col = k0 + (idx % (BK / 8)) * 8;
-    const bool ok = row >= op.row_lo && row < op.row_hi && col < klen;
-    v[i] = ok ? ld16(op.ptr + static_cast<int64_t>(row) * op.ld + col) : u32x4{0u, 0u, 0u, 0u};
-  }
-}
+template <int BM, int BN, int WM, int WN>
+struct Tile {
+  static constexpr int NW = WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 16, FN = TN / 16;
+  static constexpr int GA = BM / 16, GB = BN / 16;
+  static constexpr int LPW = (GA + GB) / NW;  // LDS-DMA instructions per wave per stage
+  static constexpr int STAGE = (BM + BN) * kRowBytes;
+  static_assert((GA + GB) % NW == 0, "16-row groups must split evenly over the waves");
+};
 
-template <int ROWS, int VPT>
-__device__ __forceinline__ void stage_store(uint16_t *lds, const u32x4 (&v)[VPT]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int idx = t + i * NTHR;
-    const int row = idx / (BK / 8);
-    const int col = (idx % (BK / 8)) * 8;
-    *reinterpret_cast<u32x4 *>(lds + row * LDSW + col) = v[i];
-  }
-}
-
-// acc[fm][fn] += A[rows of this wave] * B[tokens of this wave]^T over klen,
-// A rows from a.row0.., B rows from b.row0.. (the tile origins).
-__device__ __forceinline__ void gemm_segment(f32x4 (&acc)[4][4], const Operand &a, int arow0,
-                                             const Operand &b, int brow0, int klen,
-                                             uint16_t *ldsA, uint16_t *ldsB) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+// One staged GEMM segment: acc += A[arow0 + ..] B[brow0 + ..]^T over k-steps
+// [s_begin, s_end) of 32.  Row pointers are per load instruction, chosen by
+// the caller (already offset to the lane's chunk); a null row pointer reads
+// the zero row.  klen bounds the valid k (tail chunks read the zero row).
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
+                                        const uint16_t *const (&rp)[(BM + BN) / 16 / (WM * WN)], int klen,
+                                        int s_begin, int s_end, const uint16_t *zero_row, uint8_t *lds) {
+  using TL = Tile<BM, BN, WM, WN>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, g = lane >> 4;
-  const int nk = (klen + BK - 1) / BK;
-  u32x4 va[VPT_A], vb[VPT_B];
+  const int lchunk = (lane & 3) ^ ((lane >> 3) & 3);
+  const int nk = s_end - s_begin;
+  int ldsoff[TL::LPW];
+#pragma unroll
+  for (int q = 0; q < TL::LPW; ++q) {
+    const int gq = wave * TL::LPW + q;
+    ldsoff[q] = gq < TL::GA ? gq * 1024 : BM * kRowBytes + (gq - TL::GA) * 1024;
+  }
+  auto issue = [&](int stage, int step) {
+    const int k = step * kBK + lchunk * 8;
+#pragma unroll
+    for (int q = 0; q < TL::LPW; ++q) {
+      const uint16_t *src = (rp[q] != nullptr && k < klen) ? rp[q] + step * kBK : zero_row;
+      __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                       (lds_void *)(lds + stage * TL::STAGE + ldsoff[q]), 16, 0, 0);
+    }
+  };
+  const int swz = (g ^ ((r16 >> 1) & 3)) * 16;
+  const int aoff = (wm * TL::TM + r16) * kRowBytes + swz;
+  const int boff = BM * kRowBytes + (wn * TL::TN + r16) * kRowBytes + swz;
 
-  stage_load<BM, VPT_A>(va, a, arow0, 0, klen);
-  stage_load<BN, VPT_B>(vb, b, brow0, 0, klen);
-  stage_store<BM, VPT_A>(ldsA, va);
-  stage_store<BN, VPT_B>(ldsB, vb);
-  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < kNST - 1; ++st)
+    if (st < nk) issue(st, s_begin + st);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      stage_load<BM, VPT_A>(va, a, arow0, (kt + 1) * BK, klen);
-      stage_load<BN, VPT_B>(vb, b, brow0, (kt + 1) * BK, klen);
-    }
-    const uint16_t *sA = ldsA + cur * BM * LDSW;
-    const uint16_t *sB = ldsB + cur * BN * LDSW;
+    // this wave's loads of k-tile kt are done once at most (NST-2) tiles of
+    // loads remain outstanding; the barrier then makes every wave's part of
+    // the tile visible, and tells that stage kt-1 is no longer being read
+    if (kt + kNST - 2 < nk)
+      wait_vmcnt<(kNST - 2) * TL::LPW>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + kNST - 1 < nk) issue((kt + kNST - 1) % kNST, s_begin + kt + kNST - 1);
+    const uint8_t *sb = lds + (kt % kNST) * TL::STAGE;
+    u32x4 fa[TL::FM], fb[TL::FN];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      u32x4 fa[4], fb[4];
+    for (int i = 0; i < TL::FM; ++i) fa[i] = *reinterpret_cast<const u32x4 *>(sb + aoff + i * 16 * kRowBytes);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        fa[f] = *reinterpret_cast<const u32x4 *>(sA + (wm * 64 + f * 16 + r16) * LDSW + kk + g * 8);
-        fb[f] = *reinterpret_cast<const u32x4 *>(sB + (wn * 64 + f * 16 + r16) * LDSW + kk + g * 8);
-      }
+    for (int j = 0; j < TL::FN; ++j) fb[j] = *reinterpret_cast<const u32x4 *>(sb + boff + j * 16 * kRowBytes);
 #pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
+    for (int i = 0; i < TL::FM; ++i)
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = mfma16x16x32(fa[fm], fb[fn], acc[fm][fn]);
-    }
-    if (more) {
-      stage_store<BM, VPT_A>(ldsA + (cur ^ 1) * BM * LDSW, va);
-      stage_store<BN, VPT_B>(ldsB + (cur ^ 1) * BN * LDSW, vb);
-    }
-    __syncthreads();
+      for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
   }
+  // every wave is done with the ring before it is refilled
+  __builtin_amdgcn_s_barrier();
 }
 
-// EPI = false: plain bf16 store of the product (launch 1, Z = X V).
-// EPI = true: scale by s, add the per-child rank-r delta, store y.
-template <bool EPI>
-__global__ __launch_bounds__(NTHR) void gemm_kernel(CallDesc c, const uint16_t *zbuf, int ldz) {
-  __shared__ __attribute__((aligned(16))) uint16_t ldsA[2 * BM * LDSW];
-  __shared__ __attribute__((aligned(16))) uint16_t ldsB[2 * BN * LDSW];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+// Workgroup index -> (feature tile, token tile), XCD-major: hardware sends
+// workgroup w to XCD w % 8; XCD x is given the contiguous unit range
+// [x * per + min(x, rem), ...) so the token tiles of one feature tile run
+// together on one XCD.
+__device__ __forceinline__ void unit_of(int id, int total, int nT, int &f, int &t) {
+  const int x = id & 7, j = id >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int u = x * per + min(x, rem) + j;
+  f = u / nT;
+  t = u % nT;
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
+  using TL = Tile<BM, BN, WM, WN>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, g = lane >> 4;
-  const int m0 = blockIdx.x * BM;   // first feature row
-  const int n0 = blockIdx.y * BN;   // first token
+  const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 3) & 3);
+  int f, t;
+  unit_of(blockIdx.x, gridDim.x, a.nT, f, t);
+  const int m0 = f * BM, n0 = t * BN;
 
-  f32x4 acc[4][4];
+  f32x4 acc[TL::FM][TL::FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TL::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const Operand A{c.W0, c.K, 0, c.Ntot};
-  const Operand X{c.x, c.K, 0, c.T};
-  gemm_segment(acc, A, m0, X, n0, c.K, ldsA, ldsB);
-
-  if (EPI) {
+  // main segment row pointers: rows of A (features) then of B (tokens)
+  {
+    const uint16_t *rp[TL::LPW];
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + wm * 64 + fm * 16 + g * 4 + i;
-        const float sc = row < c.Ntot ? c.s[row] : 0.f;
-#pragma unroll
-        for (int fn = 0; fn < 4; ++fn) acc[fm][fn][i] *= sc;
+    for (int q = 0; q < TL::LPW; ++q) {
+      const int gq = wave * TL::LPW + q;
+      if (gq < TL::GA) {
+        const int row = m0 + gq * 16 + lrow;
+        rp[q] = row < a.M ? a.A + row * a.lda + lchunk * 8 : nullptr;
+      } else {
+        const int row = n0 + (gq - TL::GA) * 16 + lrow;
+        rp[q] = row < a.T ? a.B + row * a.ldb + lchunk * 8 : nullptr;
       }
-    for (int ci = 0; ci < c.nchild; ++ci) {
-      const ChildDesc &ch = c.ch[ci];
-      if (ch.rpad == 0 || m0 >= ch.row_start + ch.N || m0 + BM <= ch.row_start) continue;
-      // U rows are indexed by feature row: element (row, k) at
-      // U + (row - row_start) * rpad + k; rows outside the child are zero.
-      const Operand Uop{ch.U - static_cast<int64_t>(ch.row_start) * ch.rpad, ch.rpad, ch.row_start,
-                        ch.row_start + ch.N};
-      const Operand Zop{zbuf + ch.zoff, ldz, 0, c.T};
-      gemm_segment(acc, Uop, m0, Zop, n0, ch.rpad, ldsA, ldsB);
     }
+    segment<BM, BN, WM, WN>(acc, rp, a.K, 0, (a.K + kBK - 1) / kBK, a.zero_row, lds);
   }
 
-  // Store: this lane holds rows m0 + wm*64 + fm*16 + 4g + i, token n0 + wn*64 + fn*16 + r16.
+  if (a.mode == 1) {
+    // scale by s (rows outside [0, M) are never stored)
 #pragma unroll
-  for (int fn = 0; fn < 4; ++fn) {
-    const int tok = n0 + wn * 64 + fn * 16 + r16;
-    if (tok >= c.T) continue;
-    uint16_t *yrow = c.y + static_cast<int64_t>(tok) * c.ldy;
+    for (int i = 0; i < TL::FM; ++i) {
+      const int row = m0 + wm * TL::TM + i * 16 + g * 4;
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
+      for (int e = 0; e < 4; ++e) {
+        const float sc = row + e < a.M ? a.s[row + e] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + wm * 64 + fm * 16 + g * 4 + i;
-        if (row >= c.Ntot) continue;
-        const uint16_t out = f32_to_bf16(acc[fm][fn][i]);
-        if (!EPI) {
-          yrow[row] = out;
+        for (int j = 0; j < TL::FN; ++j) acc[i][j][e] *= sc;
+      }
+    }
+    // delta = Z U^T for every child with rows in this tile
+    for (int ci = 0; ci < a.nchild; ++ci) {
+      const ChildDesc &ch = a.ch[ci];
+      if (ch.rpad == 0 || m0 >= ch.row_start + ch.N || m0 + BM <= ch.row_start) continue;
+      const uint16_t *rp[TL::LPW];
+#pragma unroll
+      for (int q = 0; q < TL::LPW; ++q) {
+        const int gq = wave * TL::LPW + q;
+        if (gq < TL::GA) {
+          const int row = m0 + gq * 16 + lrow;
+          const bool in = row >= ch.row_start && row < ch.row_start + ch.N;
+          rp[q] = in ? ch.U + static_cast<int64_t>(row - ch.row_start) * ch.rpad + lchunk * 8 : nullptr;
         } else {
-          int ci = 0;
-          while (ci + 1 < c.nchild && row >= c.ch[ci + 1].row_start) ++ci;
-          const ChildDesc &ch = c.ch[ci];
-          const int j = row - ch.row_start;
-          yrow[ch.y_off + j] = out;
-          if (ch.dup_off >= 0) yrow[ch.dup_off + j] = out;
+          const int row = n0 + (gq - TL::GA) * 16 + lrow;
+          rp[q] = row < a.T ? a.Z + static_cast<int64_t>(row) * a.ldz + ch.zoff + lchunk * 8 : nullptr;
         }
       }
+      segment<BM, BN, WM, WN>(acc, rp, ch.rpad, 0, (ch.rpad + kBK - 1) / kBK, a.zero_row, lds);
+    }
+  }
+
+  // store: lane holds rows m0 + wm*TM + 16i + 4g + e, token n0 + wn*TN + 16j + r16
+#pragma unroll
+  for (int j = 0; j < TL::FN; ++j) {
+    const int tok = n0 + wn * TL::TN + j * 16 + r16;
+    if (tok >= a.T) continue;
+    uint16_t *yrow = a.Y + static_cast<int64_t>(tok) * a.ldy;
+#pragma unroll
+    for (int i = 0; i < TL::FM; ++i) {
+      const int row = m0 + wm * TL::TM + i * 16 + g * 4;
+      if (row >= a.M) continue;
+      uint16_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(acc[i][j][e]);
+      if (a.mode == 0) {
+        if (row + 3 < a.M && ((a.ldy | row) & 3) == 0) {
+          *reinterpret_cast<uint2 *>(yrow + row) =
+              make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (row + e < a.M) yrow[row + e] = o[e];
+        }
+      } else {
+        for (int e = 0; e < 4; ++e) {
+          const int r = row + e;
+          if (r >= a.M) break;
+          int ci = 0;
+          while (ci + 1 < a.nchild && r >= a.ch[ci + 1].row_start) ++ci;
+          const ChildDesc &ch = a.ch[ci];
+          const int jj = r - ch.row_start;
+          yrow[ch.y_off + jj] = o[e];
+          if (ch.dup_off >= 0) yrow[ch.dup_off + jj] = o[e];
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(kNST) * Tile<BM, BN, WM, WN>::STAGE;
+  auto kern = gemm_kernel<BM, BN, WM, WN>;
+  static bool attr_set = false;  // per instance; setting it twice is harmless
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(a.nM * a.nT), dim3(WM * WN * 64), lds, stream, a);
+  return hipGetLastError();
+}
+
+// Tile shapes, largest first: (BM features, BN tokens, waves).
+struct TileCfg {
+  int BM, BN;
+};
+constexpr TileCfg kTiles[] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}};
+
+// The largest tile that still gives every CU a workgroup; else the smallest.
+int pick_tile(int M, int T) {
+  constexpr int kCUs = 256;
+  const int n = sizeof(kTiles) / sizeof(kTiles[0]);
+  for (int i = 0; i < n; ++i) {
+    const long tiles = static_cast<long>((M + kTiles[i].BM - 1) / kTiles[i].BM) * ((T + kTiles[i].BN - 1) / kTiles[i].BN);
+    if (tiles >= kCUs) return i;
+  }
+  return n - 1;
+}
+
+hipError_t launch_tiled(GemmArgs a, hipStream_t stream) {
+  const int i = pick_tile(a.M, a.T);
+  a.nM = (a.M + kTiles[i].BM - 1) / kTiles[i].BM;
+  a.nT = (a.T + kTiles[i].BN - 1) / kTiles[i].BN;
+  switch (i) {
+    case 0: return launch_gemm<256, 256, 4, 2>(a, stream);
+    case 1: return launch_gemm<256, 128, 4, 2>(a, stream);
+    case 2: return launch_gemm<128, 128, 2, 2>(a, stream);
+    case 3: return launch_gemm<128, 64, 2, 2>(a, stream);
+    default: return launch_gemm<64, 64, 2, 2>(a, stream);
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, hipStream_t stream) {
-  const dim3 block(NTHR);
+hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, const uint16_t *zero_row, hipStream_t stream) {
+  hipError_t e;
   if (c.Rz > 0) {
-    CallDesc zc = c;
-    zc.W0 = c.Vt;
-    zc.Ntot = c.Rz;
-    zc.s = nullptr;
-    zc.y = zbuf;
-    zc.ldy = c.Rz;
-    zc.nchild = 1;
-    zc.ch[0] = ChildDesc{nullptr, 0, c.Rz, 0, 0, 0, -1};
-    const dim3 gz((c.Rz + BM - 1) / BM, (c.T + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_kernel<false>), gz, block, 0, stream, zc, nullptr, 0);
-    hipError_t e = hipGetLastError();
+    GemmArgs a{};
+    a.A = c.Vt;
+    a.M = c.Rz;
+    a.lda = c.K;
+    a.B = c.x;
+    a.T = c.T;
+    a.ldb = c.K;
+    a.K = c.K;
+    a.zero_row = zero_row;
+    a.mode = 0;
+    a.Y = zbuf;
+    a.ldy = c.Rz;
+    e = launch_tiled(a, stream);
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((c.Ntot + BM - 1) / BM, (c.T + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<true>), grid, block, 0, stream, c, zbuf, c.Rz);
-  return hipGetLastError();
+  GemmArgs a{};
+  a.A = c.W0;
+  a.M = c.Ntot;
+  a.lda = c.K;
+  a.B = c.x;
+  a.T = c.T;
+  a.ldb = c.K;
+  a.K = c.K;
+  a.zero_row = zero_row;
+  a.mode = 1;
+  a.Y = c.y;
+  a.ldy = c.ldy;
+  a.s = c.s;
+  a.Z = zbuf;
+  a.ldz = c.Rz;
+  a.nchild = c.nchild;
+  for (int i = 0; i < c.nchild; ++i) a.ch[i] = c.ch[i];
+  return launch_tiled(a, stream);
 }
 
 }  // namespace wl

@@ -14,14 +14,18 @@
 //       concatenated (q;k;v, gate;up), so a stacked call streams one block
 //   for each layer l, group g present on l's type:
 //       s   [sum N]          float32
-//       V^T [sum rpad, K]    bf16   (child ranks padded to a multiple of 8
+//       V^T [sum rpad, K]    bf16   (child ranks padded to a multiple of 32
 //                                    with zero rows)
 //       U   [N, rpad]        bf16, one block per child (zero pad columns)
+//
+//   a 256-byte block of zeros (read by the prefill GEMM in place of rows or
+//   k columns outside an operand)
 //
 // A stacked call therefore sees contiguous W0 rows, contiguous s, contiguous
 // V^T rows and one U block per child; a single-family call sees a row slice.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <array>
 #include <cstdarg>
 #include <cstdio>
@@ -92,6 +96,7 @@ struct Layout {
   std::vector<int64_t> w0;  // [(band * NT + tkey) * kGroups + g], -1 if absent
   std::vector<LayerOff> lay;
   size_t bytes = 0;
+  size_t zero_off = 0;  // 256 zero bytes
   int Rmax = 0;  // largest sum of padded ranks of a group
   int Nmax = 0;  // largest sum of rows of a group
 
@@ -163,7 +168,7 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
         gs.fam[c] = f;
         gs.N[c] = N;
         gs.r[c] = spec->rank[t][f];
-        gs.rpad[c] = (gs.r[c] + 7) & ~7;
+        gs.rpad[c] = (gs.r[c] + 31) & ~31;
         gs.row_start[c] = gs.Ntot;
         gs.zoff[c] = gs.Rtot;
         gs.Ntot += N;
@@ -212,6 +217,8 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
       }
     }
   }
+  lo.zero_off = off;
+  off += 256;
   lo.bytes = off;
   return WL_OK;
 }
@@ -223,12 +230,15 @@ size_t ws_p_part_bytes(const Layout &lo, int32_t T) {
   return align256(static_cast<size_t>(wl::kDecodeMaxSlices) * T * lo.Nmax * 4);
 }
 
+// Prefill (T > 16): Z [T][Rmax] bf16.
+size_t ws_prefill_z_bytes(const Layout &lo, int32_t T) { return align256(static_cast<size_t>(T) * lo.Rmax * 2); }
+
 size_t ws_bytes_for(const Layout &lo, int32_t T) {
   size_t n;
   if (T <= wl::kDecodeMaxT)
     n = ws_p_part_bytes(lo, T) + align256(static_cast<size_t>(T) * lo.Rmax * 4);
   else
-    n = align256(static_cast<size_t>(T) * lo.Rmax * 2);
+    n = ws_prefill_z_bytes(lo, T);
   return n < 256 ? 256 : n;
 }
 
@@ -344,7 +354,7 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
   if (T <= wl::kDecodeMaxT)
     e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), reinterpret_cast<float *>(ws + ws_p_part_bytes(h->lo, T)), s);
   else
-    e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws), s);
+    e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws), reinterpret_cast<const uint16_t *>(h->arena + h->lo.zero_off), s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return WL_OK;
 }
