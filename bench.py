@@ -130,10 +130,15 @@ def time_graph(step, steps, warmup):
 def time_launches(step, reps):
     """Per-call-type average duration with HIP events recorded on the launch
     stream around each call, in step order (so W0 re-reads across layers see
-    the same cache state as in the step)."""
+    the same cache state as in the step).  The GPU is first parked on a short
+    spin so the host enqueues every call before the GPU reaches them: the
+    event pairs then bracket GPU work only, not host launch gaps."""
     import torch
     names = list(step.per_call)
     evs = []
+    torch.cuda.synchronize()
+    # ~60 us of host enqueue work per call; spin the GPU that long (2.4 GHz)
+    torch.cuda._sleep(int(2.4e9 * 60e-6 * len(step.items) * reps) + 10_000_000)
     for _ in range(reps):
         for layer, name, stacked, x, y in step.items:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -161,18 +166,19 @@ def source_sha(*names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_file, sha, launches_per_unit):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel source; else None."""
+def traffic_from_profile(key, sha):
+    """HBM bytes per call from the committed rocprofv3 counter summary
+    (profiles/counters.json), if it was taken on the current kernel source;
+    else None."""
     p = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    rec = d.get(kernel_file)
+    rec = d.get(key)
     if not rec or rec.get("source_sha") != sha:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_call")
 
 
 def decode_section(wl, T, steps, warmup, dev, reps=3):
@@ -217,7 +223,9 @@ def prefill_section(wl, T, calls, steps, warmup, dev, reps=1):
     kern_time = sum(durs[n] * pc["calls"] for n, pc in step.per_call.items())
     out = {"step_s": t_step, "flops": step.flops, "TFLOPs": step.flops / t_step / 1e12,
            "mfma_frac": step.flops / t_step / 1e12 / BF16_PEAK_TFLOPS,
-           "call_TFLOPs": step.flops / kern_time / 1e12, "calls": launches, "per_call": per_call}
+           "call_TFLOPs": step.flops / kern_time / 1e12, "calls": launches,
+           "avg_call_us": kern_time / launches * 1e6, "flops_per_call": step.flops / launches,
+           "per_call": per_call}
     del g, step, bundle
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -259,14 +267,112 @@ def cpu_baseline(wl, T, budget_s, dev):
                       f"bundle bytes), repeated {n}x in {el:.1f} s; W0/s/U/V pre-upcast to fp64 outside the timing"}
 
 
+def band_reuse(dev, reps=5):
+    """Band reuse of W0 (decode, T=1).  For two consecutive layers l, l+1 of
+    one band, the second call reads the same W0 bytes as the first.  Three
+    timings per call type, each the median over reps, GPU time from HIP
+    events with the GPU parked so host gaps do not count:
+      cold:   Infinity Cache flushed (1 GiB written), then the call on layer l
+      reuse:  the call on layer l+1 issued right after the call on layer l
+      model:  the call on layer l+1 when every call of layer l ran in
+              between (model order)
+      repeat: the call on layer l issued right after the same call (everything
+              it reads was just read)
+    A re-read served by the 256 MB Infinity Cache shows as an effective rate
+    above the cold (HBM) rate.  Bytes are the call's algorithmic read bytes."""
+    import statistics
+    import torch
+    import synth
+    import synth.device as sdev
+    flush_buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)   # 1 GiB, read to evict
+
+    class _Flush:
+        def zero_(self):
+            flush_buf.sum()    # reads 1 GiB (4x the Infinity Cache), writes nothing large
+    flush = _Flush()
+    out = {"method": "median GPU time over %d reps; before each cold measurement 1 GiB is read (a read-only "
+                     "pass, so no dirty lines are left to write back)" % reps, "cases": []}
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        return e0, e1
+
+    for wl, layer in ((synth.workload(1), 0), (synth.custom(26, 13, 32, dict(synth.workload(2).dims), cid=2), 0),
+                      (synth.workload(4), 0)):
+        bundle = sdev.load(wl, dev)
+        calls = [c for c in CALLS if all((0, f) in wl.dims for f in c[1])] or [("up", ("up",))]
+        if wl.cid == 1:
+            calls = [("up", ("up",))]
+        xs = {(l, c): wl.x(l, c, 1, dev) for l in (layer, layer + 1) for c, _ in calls}
+        ws = bundle.workspace(1)
+
+        def run(l, c):
+            x = xs[(l, c)]
+            return (lambda: bundle.stacked(l, c, x, ws=ws)) if c in ("qkv", "gate_up") else \
+                (lambda: bundle.linear(l, c, x, ws=ws))
+        for c, fams in calls:
+            nbytes = call_bytes(wl, layer + 1, list(fams), 1)[0]
+            w0 = sum(2 * wl.shape(0, f)[0] * wl.shape(0, f)[1] for f in fams)
+            cold, reuse, model, repeat = [], [], [], []
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                flush.zero_()
+                torch.cuda._sleep(20_000_000)
+                ev_cold = timed(run(layer, c))
+                ev_reuse = timed(run(layer + 1, c))
+                torch.cuda.synchronize()
+                cold.append(ev_cold[0].elapsed_time(ev_cold[1]) * 1e-3)
+                reuse.append(ev_reuse[0].elapsed_time(ev_reuse[1]) * 1e-3)
+                flush.zero_()
+                torch.cuda._sleep(20_000_000)
+                for c2, _ in calls:
+                    run(layer, c2)()
+                for c2, _ in calls:
+                    if c2 == c:
+                        break
+                    run(layer + 1, c2)()
+                ev_model = timed(run(layer + 1, c))
+                torch.cuda.synchronize()
+                model.append(ev_model[0].elapsed_time(ev_model[1]) * 1e-3)
+                torch.cuda._sleep(20_000_000)
+                run(layer, c)()
+                ev_rep = timed(run(layer, c))
+                torch.cuda.synchronize()
+                repeat.append(ev_rep[0].elapsed_time(ev_rep[1]) * 1e-3)
+            tc, tr, tm, tp = (statistics.median(v) for v in (cold, reuse, model, repeat))
+            between = sum(2 * wl.shape(0, f)[0] * wl.shape(0, f)[1] for c2, fs in calls if c2 != c for f in fs)
+            out["cases"].append({
+                "workload": wl.name, "call": c, "layers": [layer, layer + 1], "same_band": wl.band(layer) == wl.band(layer + 1),
+                "w0_MB": w0 / 1e6, "bytes_read_MB": nbytes / 1e6, "other_w0_between_in_model_order_MB": between / 1e6,
+                "cold_us": tc * 1e6, "reuse_us": tr * 1e6, "model_order_us": tm * 1e6, "same_layer_repeat_us": tp * 1e6,
+                "cold_GBps": nbytes / tc / 1e9, "reuse_GBps": nbytes / tr / 1e9, "model_order_GBps": nbytes / tm / 1e9,
+                "same_layer_repeat_GBps": nbytes / tp / 1e9,
+                "reuse_served_by_infinity_cache": tr < 0.8 * tc,
+                "model_order_served_by_infinity_cache": tm < 0.8 * tc})
+            log(f"band reuse {wl.name} {c}: cold {tc*1e6:.1f} us, reuse {tr*1e6:.1f} us, model order {tm*1e6:.1f} us, "
+                f"repeat {tp*1e6:.1f} us")
+        del bundle
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--only", default="all", choices=["all", "decode", "prefill"])
+    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill"])
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--band-reuse", action="store_true",
+                    help="report whether a band-shared W0 re-read by the next layer is served from the 256 MB "
+                         "Infinity Cache or from HBM (prints one JSON line)")
+    ap.add_argument("--profile", action="store_true",
+                    help="for rocprofv3 counter runs: one eager decode step of the headline workload, then a "
+                         "plain 1 GiB device copy whose counters calibrate FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the weightless linear here runs on a single MI355X "
@@ -281,11 +387,29 @@ def main():
     from weight_shared_rank_amd import binding
     binding.lib()
 
-    res = {}
     wl4 = synth.workload(4)
-    if args.only in ("all", "decode"):
+    if args.profile:
+        import synth.device as sdev
+        bundle = sdev.load(wl4, dev)
+        step = Step(wl4, bundle, 1, CALLS, dev)
+        step.run()
+        torch.cuda.synchronize()
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "done", "bytes_per_call": step.bytes_rd / len(step.items),
+                          "calls": len(step.items), "copy_bytes": src.numel() * 2}), flush=True)
+        return
+
+    res = {}
+    if args.band_reuse:
+        print(json.dumps(band_reuse(dev)), flush=True)
+        return
+    if args.only in ("all", "decode", "decode1"):
         res["decode4_t1"] = decode_section(wl4, 1, args.steps, args.warmup, dev)
         log(f"decode T=1: {res['decode4_t1']['GBps']:.1f} GB/s")
+    if args.only in ("all", "decode"):
         res["decode4_t16"] = decode_section(wl4, 16, args.steps, args.warmup, dev)
         log(f"decode T=16: {res['decode4_t16']['GBps']:.1f} GB/s")
         res["decode2_t1"] = decode_section(synth.custom(26, 13, 32, dict(synth.workload(2).dims), cid=2),
@@ -310,18 +434,31 @@ def main():
                                 "tokens": 1, "layers": 60, "bands": 5, "rank": 256,
                                 "bytes_read_per_step": d["bytes_read"], "hbm_frac": d["GBps"] / HBM_PEAK_GBS}})
         sha = source_sha("decode.hip", "common.h", "internal.h")
-        line["roofline"] = {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(d["kernel_GBps"], 2),
-                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        line["roofline"] = {"bound": "hbm",
+                            "kernel": "stream_kernel + epilogue_kernel (one decode call is these two launches; "
+                                      "the stream launch moves ~95% of the bytes)",
+                            "achieved": round(d["kernel_GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(d["kernel_GBps"] / HBM_PEAK_GBS, 4),
-                            "bytes_per_launch": d["bytes_per_launch"], "avg_launch_us": round(d["avg_launch_us"], 3),
-                            "traffic": traffic_from_profile("decode.hip", sha, 1), "source_sha": sha}
+                            "bytes_per_call": d["bytes_per_launch"], "avg_call_us": round(d["avg_launch_us"], 3),
+                            "traffic": traffic_from_profile("decode", sha), "source_sha": sha}
     line["detail"] = res
     if "prefill5" in res:
         p = res["prefill5"]
+        psha = source_sha("prefill.hip", "common.h", "internal.h")
         line["prefill"] = {"metric": "prefill TFLOP/s", "value": round(p["TFLOPs"], 2), "unit": "TFLOP/s",
                            "mfma_frac": round(p["mfma_frac"], 4), "peak": BF16_PEAK_TFLOPS,
+                           "ms_per_step": round(p["step_s"] * 1e3, 3),
                            "workload": "gemma4-31b mixed prefill: 10 full + 50 sliding layers, G=1 per type, "
-                                       "rank 1024, T=512, graph-replayed step"}
+                                       "rank 1024, T=512, graph-replayed step",
+                           "roofline": {"bound": "mfma",
+                                        "kernel": "gemm_kernel (Z = X V, then the main GEMM with the fused s and "
+                                                  "U z epilogue: two launches per call)",
+                                        "achieved": round(p["call_TFLOPs"], 2), "peak": BF16_PEAK_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": round(p["call_TFLOPs"] / BF16_PEAK_TFLOPS, 4),
+                                        "flops_per_call": p["flops_per_call"], "avg_call_us": round(p["avg_call_us"], 2),
+                                        "traffic": traffic_from_profile("prefill", psha), "source_sha": psha}}
+        if "prefill3" in res:
+            line["prefill"]["gemma3_1b_T2048_TFLOPs"] = round(res["prefill3"]["TFLOPs"], 2)
     if not args.no_cpu and args.only in ("all", "decode"):
         log("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(wl4, 1, args.cpu_budget, dev)

@@ -59,7 +59,7 @@ def lib():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIBPATH):
-        raise RuntimeError(f"{LIBPATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        raise RuntimeError(f"{LIBPATH} is not built; run `python -m weight_shared_rank_amd.build`")
     L = ctypes.CDLL(LIBPATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sig = {
