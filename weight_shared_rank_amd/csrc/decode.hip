@@ -18,13 +18,14 @@
 //     B operand (token columns >= T are zero, so T = 1 and T = 16 run the same
 //     code).  The waves' sums are reduced through LDS in a fixed order and the
 //     fp32 partial of the tile is written for tokens < T: p_part[slice][t][row]
-//     for W0 rows, z_part[t][rank] for V^T rows.
+//     for W0 rows.  V^T rows hold all of z = V^T x; they store it as a bf16
+//     pair, z_hi[t][rank] = bf16(z) and z_lo[t][rank] = bf16(z - z_hi), which
+//     keeps ~16 significant bits and is the MFMA operand of launch 2.
 //     The V^T tiles are not split (z needs no summation) and come first in
 //     the grid, so they are dispatched early and end well inside the launch.
 //   launch 2 (epilogue_kernel): one workgroup per 16-row tile.  Its waves
-//     split the rank steps of U z: each splits z into a bf16 hi part and a
-//     bf16 lo remainder (z keeps ~16 significant bits) and runs two MFMAs per
-//     32 ranks with U rows as the A operand; the waves' sums are reduced
+//     split the rank steps of U z: two MFMAs per 32 ranks (z_hi, then z_lo,
+//     as B operands) with U rows as the A operand; the waves' sums are reduced
 //     through LDS, the KS partials of p are summed in slice order, scaled by
 //     s, and y is written once in bf16.  It reads U (r/K of W0's bytes) and
 //     the partials.
@@ -40,9 +41,23 @@ namespace wl {
 
 namespace {
 
-constexpr int kStreamWaves = 8;
-constexpr int kStreamUnroll = 4;
-constexpr int kEpiWaves = 4;
+// Launch shape (overridable at build time for tuning sweeps).
+#ifndef WL_STREAM_WAVES
+#define WL_STREAM_WAVES 8
+#endif
+#ifndef WL_STREAM_UNROLL
+#define WL_STREAM_UNROLL 4
+#endif
+#ifndef WL_EPI_WAVES
+#define WL_EPI_WAVES 4
+#endif
+#ifndef WL_DECODE_TARGET_WGS
+#define WL_DECODE_TARGET_WGS 4096
+#endif
+constexpr int kStreamWaves = WL_STREAM_WAVES;
+constexpr int kStreamUnroll = WL_STREAM_UNROLL;
+constexpr int kEpiWaves = WL_EPI_WAVES;
+constexpr int kTargetWgs = WL_DECODE_TARGET_WGS;
 
 // One batch of UNROLL complete k-steps (32 k each): loads first, then MFMAs.
 template <int UNROLL>
@@ -67,7 +82,7 @@ __device__ __forceinline__ void kblock(f32x4 &acc, const uint16_t *arow, const u
 // are dispatched first and finish well inside the launch), then the W0 tiles,
 // each split into KS slices of K.
 template <int W, int UNROLL>
-__global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_part, float *z_part, int ntile_vt,
+__global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_part, uint16_t *z_pair, int ntile_vt,
                                                         int KS) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
@@ -110,8 +125,21 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
 #pragma unroll
   for (int w = 1; w < W; ++w) tot += red[w][lane];
   // lane holds D[m = 4g + i][n = r16]: rows row0 + 4g + i, token r16
-  const int ld = vt ? c.Rz : c.Ntot;
-  float *dst = (vt ? z_part : p_part) + (static_cast<size_t>(slice) * c.T + r16) * ld;
+  if (vt) {
+    uint16_t *zh = z_pair + static_cast<size_t>(r16) * c.Rz;
+    uint16_t *zl = zh + static_cast<size_t>(c.T) * c.Rz;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + g * 4 + i;
+      if (row < nrows) {
+        const uint16_t hi = f32_to_bf16(tot[i]);
+        zh[row] = hi;
+        zl[row] = f32_to_bf16(tot[i] - bf16_to_f32(hi));
+      }
+    }
+    return;
+  }
+  float *dst = p_part + (static_cast<size_t>(slice) * c.T + r16) * c.Ntot;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = row0 + g * 4 + i;
@@ -119,28 +147,9 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
   }
 }
 
-// z B-fragment: ranks k .. k+7 of token r16 as a bf16 hi/lo pair.
-__device__ __forceinline__ void z_fragment(const float *z_part, int Rz, int r16, int k, bool valid, u32x4 &hi,
-                                           u32x4 &lo) {
-  f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-  if (valid) {
-    const float *p = z_part + static_cast<size_t>(r16) * Rz + k;
-    a = *reinterpret_cast<const f32x4 *>(p);
-    b = *reinterpret_cast<const f32x4 *>(p + 4);
-  }
-  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint16_t h0 = f32_to_bf16(v[2 * e]), h1 = f32_to_bf16(v[2 * e + 1]);
-    const uint16_t l0 = f32_to_bf16(v[2 * e] - bf16_to_f32(h0)), l1 = f32_to_bf16(v[2 * e + 1] - bf16_to_f32(h1));
-    hi[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-    lo[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
-  }
-}
-
 // One workgroup per 16-row tile; its WE waves split the rank steps of U z.
 template <int WE>
-__global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const float *p_part, const float *z_part,
+__global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const float *p_part, const uint16_t *z_pair,
                                                            int KS) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
@@ -149,21 +158,28 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   const int rbase = row0 + g * 4;
 
-  // wave 0 starts the loads of the p partials (this lane: rows rbase..+3,
-  // token r16) before the delta
-  f32x4 p = {0.f, 0.f, 0.f, 0.f};
+  // wave 0 loads the p partials and s of this lane's rows rbase..+3, token
+  // r16; they are summed (in slice order) only after the delta, so these
+  // loads and those of U and z are in flight together.  Slices past KS and
+  // rows past Ntot re-read a valid address and are dropped.
+  f32x4 part[kDecodeMaxSlices];
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
   if (wave == 0 && tok_ok) {
-    if (rbase + 3 < c.Ntot && (c.Ntot & 3) == 0) {
-      const float *pp = p_part + static_cast<size_t>(r16) * c.Ntot + rbase;
-      for (int s = 0; s < KS; ++s) {
-        p += *reinterpret_cast<const f32x4 *>(pp);
-        pp += static_cast<size_t>(c.T) * c.Ntot;
-      }
-    } else {
-      for (int s = 0; s < KS; ++s)
+    const size_t sstride = static_cast<size_t>(c.T) * c.Ntot;
+    const float *pp = p_part + static_cast<size_t>(r16) * c.Ntot;
+    if (rbase + 3 < c.Ntot && (c.Ntot & 3) == 0 && (reinterpret_cast<uintptr_t>(c.s) & 15) == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (rbase + i < c.Ntot) p[i] += p_part[(static_cast<size_t>(s) * c.T + r16) * c.Ntot + rbase + i];
+      for (int s = 0; s < kDecodeMaxSlices; ++s)
+        part[s] = *reinterpret_cast<const f32x4 *>(pp + static_cast<size_t>(min(s, KS - 1)) * sstride + rbase);
+      sc = *reinterpret_cast<const f32x4 *>(c.s + rbase);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(rbase + i, c.Ntot - 1);
+#pragma unroll
+        for (int s = 0; s < kDecodeMaxSlices; ++s) part[s][i] = pp[static_cast<size_t>(min(s, KS - 1)) * sstride + row];
+        sc[i] = c.s[row];
+      }
     }
   }
 
@@ -176,18 +192,25 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
     if (ch.rpad == 0 || row0 >= ch.row_start + ch.N || row0 + 16 <= ch.row_start) continue;
     const bool in_child = arow_g >= ch.row_start && arow_g < ch.row_start + ch.N;
     const uint16_t *urow = ch.U + static_cast<size_t>(in_child ? arow_g - ch.row_start : 0) * ch.rpad + g * 8;
+    // z pair row of this lane's token (token 0 stands in for columns >= T)
+    const uint16_t *zh = z_pair + static_cast<size_t>(tok_ok ? r16 : 0) * c.Rz + ch.zoff + g * 8;
+    const uint16_t *zl = zh + static_cast<size_t>(c.T) * c.Rz;
+    // kk and k1 are multiples of 32 and rpad is too, so a step is either
+    // wholly inside the padded rank or wholly outside.  Every load is
+    // unconditional (an outside step re-reads step kk) and issued before the
+    // MFMAs, so all of a wave's loads are in flight together.
     for (int kk = wave * 32; kk < ch.rpad; kk += 2 * WE * 32) {
       const int k1 = kk + WE * 32;
-      const bool in0 = kk + g * 8 < ch.rpad, in1 = k1 + g * 8 < ch.rpad;
-      const u32x4 a0 = (in0 && in_child) ? ld16(urow + kk) : zero4;
-      const u32x4 a1 = (in1 && in_child) ? ld16(urow + k1) : zero4;
-      u32x4 h0, l0, h1, l1;
-      z_fragment(z_part, c.Rz, r16, ch.zoff + kk + g * 8, in0 && tok_ok, h0, l0);
-      z_fragment(z_part, c.Rz, r16, ch.zoff + k1 + g * 8, in1 && tok_ok, h1, l1);
-      dacc = mfma16x16x32(a0, h0, dacc);
-      dacc = mfma16x16x32(a0, l0, dacc);
-      dacc = mfma16x16x32(a1, h1, dacc);
-      dacc = mfma16x16x32(a1, l1, dacc);
+      const bool in1 = k1 < ch.rpad;
+      const int k1c = in1 ? k1 : kk;
+      const u32x4 ua0 = ld16(urow + kk), ua1 = ld16(urow + k1c);
+      const u32x4 h0 = ld16(zh + kk), l0 = ld16(zl + kk), h1 = ld16(zh + k1c), l1 = ld16(zl + k1c);
+      const u32x4 a0 = in_child ? ua0 : zero4;
+      const u32x4 a1 = (in1 && in_child) ? ua1 : zero4;
+      dacc = mfma16x16x32(a0, tok_ok ? h0 : zero4, dacc);
+      dacc = mfma16x16x32(a0, tok_ok ? l0 : zero4, dacc);
+      dacc = mfma16x16x32(a1, (in1 && tok_ok) ? h1 : zero4, dacc);
+      dacc = mfma16x16x32(a1, (in1 && tok_ok) ? l1 : zero4, dacc);
     }
   }
   __shared__ f32x4 red[WE][64];
@@ -197,6 +220,10 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
   f32x4 d = red[0][lane];
 #pragma unroll
   for (int w = 1; w < WE; ++w) d += red[w][lane];
+  f32x4 p = part[0];
+#pragma unroll
+  for (int s = 1; s < kDecodeMaxSlices; ++s)
+    if (s < KS) p += part[s];
 
   // lane holds D[m = 4g + i][n = r16]: rows rbase + i, token r16
   uint16_t *yrow = c.y + static_cast<size_t>(r16) * c.ldy;
@@ -207,7 +234,7 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
     int ci = 0;
     while (ci + 1 < c.nchild && row >= c.ch[ci + 1].row_start) ++ci;
     const ChildDesc &ch = c.ch[ci];
-    const uint16_t out = f32_to_bf16(c.s[row] * p[i] + d[i]);
+    const uint16_t out = f32_to_bf16(sc[i] * p[i] + d[i]);
     const int j = row - ch.row_start;
     yrow[ch.y_off + j] = out;
     if (ch.dup_off >= 0) yrow[ch.dup_off + j] = out;
@@ -217,24 +244,24 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
 }  // namespace
 
 int decode_k_slices(int Ntot, int Rz, int K) {
-  // Aim for about 4096 workgroups in the stream launch, with K slices of at
-  // least 16 k-steps and at most kDecodeMaxSlices slices.
+  // Aim for about kTargetWgs workgroups in the stream launch, with K slices
+  // of at least 16 k-steps and at most kDecodeMaxSlices slices.
   const int tiles = (Ntot + 15) / 16 + (Rz + 15) / 16;
   const int nsteps = (K + 31) / 32;
-  int ks = (4096 + tiles - 1) / max(1, tiles);
+  int ks = (kTargetWgs + tiles - 1) / max(1, tiles);
   ks = min(ks, max(1, nsteps / 16));
   return max(1, min(ks, kDecodeMaxSlices));
 }
 
-hipError_t launch_decode(const CallDesc &c, float *p_part, float *z_part, hipStream_t stream) {
+hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream) {
   const int KS = decode_k_slices(c.Ntot, c.Rz, c.K);
   const int nt_w0 = (c.Ntot + 15) / 16, nt_vt = (c.Rz + 15) / 16;
   hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nt_vt + nt_w0 * KS), dim3(kStreamWaves * 64),
-                     0, stream, c, p_part, z_part, nt_vt, KS);
+                     0, stream, c, p_part, z_pair, nt_vt, KS);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((epilogue_kernel<kEpiWaves>), dim3(nt_w0), dim3(kEpiWaves * 64), 0, stream, c,
-                     static_cast<const float *>(p_part), static_cast<const float *>(z_part), KS);
+                     static_cast<const float *>(p_part), static_cast<const uint16_t *>(z_pair), KS);
   return hipGetLastError();
 }
 

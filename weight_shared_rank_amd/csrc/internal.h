@@ -13,7 +13,10 @@ constexpr int kMaxChildren = 3;
 
 // Decode path: the stream launch splits K into at most kDecodeMaxSlices
 // slices and writes fp32 partials [slice][token][row] of W0 x and V^T x.
-constexpr int kDecodeMaxSlices = 8;
+#ifndef WL_DECODE_MAX_SLICES
+#define WL_DECODE_MAX_SLICES 8
+#endif
+constexpr int kDecodeMaxSlices = WL_DECODE_MAX_SLICES;
 
 // One child projection of a (possibly stacked) call, as the kernels see it.
 struct ChildDesc {
@@ -39,10 +42,11 @@ struct CallDesc {
 };
 
 // Decode path (T <= 16): launch 1 streams [W0; V^T] x into the K-slice
-// partials p_part [KS][T][Ntot] and z_part [T][Rz] (V^T rows are not split);
-// launch 2 sums the partials and applies the scale and the U z epilogue.
+// partials p_part [KS][T][Ntot] (fp32) and z = V^T x (V^T rows are not
+// split) as a bf16 hi/lo pair z_pair [2][T][Rz]; launch 2 sums the partials
+// and applies the scale and the U z epilogue.
 int decode_k_slices(int Ntot, int Rz, int K);
-hipError_t launch_decode(const CallDesc &c, float *p_part, float *z_part, hipStream_t stream);
+hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream);
 
 // Prefill path (T > 16): launch 1 computes Z = X V into zbuf [T][Rz] (bf16),
 // launch 2 the main GEMM with the scale and rank-r epilogue.  zero_row points

@@ -224,7 +224,7 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
 }
 
 // Workspace.  Decode (T <= 16): the stream launch's fp32 partials,
-// p_part [kDecodeMaxSlices][T][Nmax] then z_part [T][Rmax].
+// p_part [kDecodeMaxSlices][T][Nmax] (fp32) then z_pair [2][T][Rmax] (bf16).
 // Prefill (T > 16): Z = X V as bf16 [T][Rmax].
 size_t ws_p_part_bytes(const Layout &lo, int32_t T) {
   return align256(static_cast<size_t>(wl::kDecodeMaxSlices) * T * lo.Nmax * 4);
@@ -352,7 +352,7 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
   uint8_t *ws = static_cast<uint8_t *>(d_ws);
   hipError_t e;
   if (T <= wl::kDecodeMaxT)
-    e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), reinterpret_cast<float *>(ws + ws_p_part_bytes(h->lo, T)), s);
+    e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), reinterpret_cast<uint16_t *>(ws + ws_p_part_bytes(h->lo, T)), s);
   else
     e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws), reinterpret_cast<const uint16_t *>(h->arena + h->lo.zero_off), s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
