@@ -48,10 +48,14 @@ struct CallDesc {
 int decode_k_slices(int Ntot, int Rz, int K);
 hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream);
 
-// Prefill path (T > 16): launch 1 computes Z = X V into zbuf [T][Rz] (bf16),
-// launch 2 the main GEMM with the scale and rank-r epilogue.  zero_row points
-// at >= 16 zero bytes (used to mask rows and k columns outside an operand).
-hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, const uint16_t *zero_row, hipStream_t stream);
+// Prefill path (T > 16): Z = X V into zbuf [T][Rz] (bf16), then the main
+// GEMM with the scale and rank-r epilogue.  GEMMs with few rows split K and
+// use pbuf for fp32 partials (prefill_partial_bytes bytes for this call
+// shape).  zero_row points at >= 16 zero bytes (used to mask rows and k
+// columns outside an operand).
+size_t prefill_partial_bytes(int Ntot, int Rz, int K, int T);
+hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const uint16_t *zero_row,
+                          hipStream_t stream);
 
 // Load-time helpers.
 hipError_t launch_fill_zero(void *dst, size_t bytes, hipStream_t stream);

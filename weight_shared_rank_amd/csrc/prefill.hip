@@ -1,8 +1,8 @@
-// Prefill-path kernels (T > 16 tokens): two launches of one bf16 MFMA GEMM.
+// Prefill-path kernels (T > 16 tokens): bf16 MFMA GEMMs.
 //
-//   launch 1:  Z[T, Rz] = X[T, K] V              (the thin reduction, bf16 out)
-//   launch 2:  Y[T, N]  = (X W0^T) (.) s + Z U^T   (scale and rank-r delta fused
-//              into the epilogue of the shared-block GEMM; y written once)
+//   Z[T, Rz] = X[T, K] V                          (the thin reduction, bf16)
+//   Y[T, N]  = (X W0^T) (.) s + Z U^T               (scale and rank-r delta in
+//              the epilogue of the shared-block GEMM; y written once)
 //
 // The forward is the theta-bundle forward ("Add a new model architecture"
 // page, introduction); as in the pages' GEMM formulation the operands stay
@@ -11,34 +11,42 @@
 //
 // GEMM core (gfx950).  A workgroup owns a BM x BN output tile: BM weight rows
 // ("features", MFMA A operand) by BN tokens (B operand).  Both operands are
-// K-contiguous rows.  Tiles of 32 k are moved global -> LDS by
-// global_load_lds_dwordx4 (no VGPR staging) into an NST-stage ring, so loads
-// run NST-1 k-tiles ahead of the MFMAs.  Each wave instruction fills 16
-// rows x 64 bytes (1 KB, lane i at byte 16 i); a lane fetches 16-byte chunk
-// c = (i % 4) ^ ((i / 8) % 4) of row i / 4.  This XOR-swizzles the LDS rows
-// (slot = chunk ^ ((row / 2) % 4)) so that each 8-lane phase of a 16-byte
-// fragment read (8 consecutive rows, one chunk) covers the 32 LDS banks
-// exactly once: no bank conflicts.  Lanes whose row or k lies outside the operand fetch a row of zeros
-// kept in the arena, which is how tails and foreign rows are masked (an LDS
-// DMA lane cannot be zero-filled).  Large tiles use eight waves (two per
-// SIMD, 64 x 128 or 64 x 64 each), small ones four.
+// K-contiguous rows.  Stages of 64 k (128 bytes per row) move global -> LDS by
+// global_load_lds_dwordx4 (no VGPR staging) into an NST-stage ring.  One wave
+// instruction fills 8 rows x 128 bytes: lane i writes LDS slot i % 8 of row
+// i / 8 and fetches 16-byte chunk c = (i % 8) ^ (row % 8) of that row, so
+// chunk c of row r sits in slot c ^ (r % 8).  A 16-byte fragment read (8
+// lanes per LDS phase: 8 consecutive rows, one chunk) then touches 8
+// different slots, i.e. all 32 banks once.  Whole 128-byte rows per request
+// halve the per-CU request count of 64-byte rows, and the request rate per CU,
+// not the MFMA rate, is what bounds the operand stream at a few hundred
+// tokens.  Lanes whose row or k lies outside the operand fetch a row of zeros
+// kept in the arena (an LDS-DMA lane cannot be zero-filled).
 //
-// Scheduling.  Workgroups are numbered XCD-major: hardware assigns
-// workgroup w to XCD w % 8, and the tile order is remapped so that each XCD
-// walks a contiguous range of (feature tile, K slice, token tile), token tile
-// fastest: the token tiles that share a block of W0 run at the same time on
-// one XCD and read it from HBM once (later reads hit that XCD's L2).
-// Each launch takes the largest tile shape (256x256 down to 64x64) that
-// still gives every CU a workgroup.  K is never split across workgroups:
-// combining partial tiles across XCDs needs device-scope release/acquire,
-// which on this part writes back / invalidates a whole L2 and costs more than
-// the smaller tile.
+// Scheduling.  Workgroups are numbered XCD-major: hardware assigns workgroup
+// w to XCD w % 8, and the unit order is remapped so that each XCD walks a
+// contiguous range of (feature tile, K slice, token tile), token tile
+// fastest: the token tiles that share a block of W0 run together on one XCD
+// and read it from HBM once (later reads hit that XCD's L2).
 //
-// Epilogue of launch 2: the fp32 accumulators are scaled by s per feature
-// row, then the same staged loop runs over the ranks of every child whose
-// rows meet the tile (A = that child's U rows, other rows read the zero row;
-// B = the child's columns of Z), so U z is added at MFMA rate before y is
-// rounded to bf16 and stored.
+// Tile and split choice (plan_gemm).  Big tiles (256 x 128 on eight waves)
+// stream the fewest bytes per flop and win when they fill the chip; GEMMs
+// with few rows (o, down, and Z = X V) split K into KS slices instead, so
+// that every CU streams.  Slices write fp32 partial tiles to the workspace;
+// a later launch sums them in slice order (deterministic): a reduce kernel
+// for Z, and for the main GEMM a "finish" launch of the same tiles that
+// starts from s (.) sum(P) and runs the delta.  Partials are combined across
+// launches, never across workgroups of one launch: that would need
+// device-scope release/acquire, which writes back / invalidates a whole L2
+// on this part.
+//
+// Epilogue of the main GEMM: the fp32 accumulators are scaled by s per
+// feature row, then the same staged loop runs over the ranks of every child
+// whose rows meet the tile (A = that child's U rows, other rows read the
+// zero row; B = the child's columns of Z), so U z is added at MFMA rate
+// before y is rounded to bf16 and stored.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -48,14 +56,23 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kNST = 4;       // LDS ring stages
-constexpr int kBK = 32;       // k per stage
-constexpr int kRowBytes = 64; // kBK bf16 per LDS row
+constexpr int kBK = 64;         // k per stage
+constexpr int kRowBytes = 128;  // kBK bf16 per LDS row
+constexpr int kMinSliceSteps = 8;
+constexpr int kMaxSplit = 16;
+constexpr int kCUs = 256;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
+
+enum Mode : int32_t {
+  kStoreBf16 = 0,  // Y = bf16(acc), [T][ldy]
+  kFused = 1,      // Y = child map of bf16(s (.) acc + Z U^T)
+  kPartial = 2,    // P[slice][T][M] = acc (fp32)
+  kFinish = 3,     // Y = child map of bf16(s (.) sum_slices P + Z U^T)
+};
 
 struct GemmArgs {
   // main segment: rows of A (weights) against rows of B (tokens), K long
@@ -68,42 +85,45 @@ struct GemmArgs {
   int32_t K;
   const uint16_t *zero_row;  // >= 16 zero bytes
   // tiling
-  int32_t nM, nT;     // feature tiles, token tiles
+  int32_t nM, nT, ksplit, steps_per_slice;
   // epilogue
-  int32_t mode;       // 0: Y = bf16(acc) [T][ldy]; 1: scale + delta + child map
+  int32_t mode;
   uint16_t *Y;
   int32_t ldy;
   const float *s;
-  const uint16_t *Z;  // [T][ldz] (mode 1)
+  const uint16_t *Z;  // [T][ldz]
   int32_t ldz;
+  float *P;           // partials [ksplit][T][M]
   int32_t nchild;
   ChildDesc ch[kMaxChildren];
 };
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NST>
 struct Tile {
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
-  static constexpr int GA = BM / 16, GB = BN / 16;
-  static constexpr int LPW = (GA + GB) / NW;  // LDS-DMA instructions per wave per stage
+  static constexpr int GA = BM / 8, GB = BN / 8;  // 8-row load groups
+  static constexpr int LPW = (GA + GB) / NW;      // LDS-DMA instructions per wave per stage
   static constexpr int STAGE = (BM + BN) * kRowBytes;
-  static_assert((GA + GB) % NW == 0, "16-row groups must split evenly over the waves");
+  static constexpr size_t LDS = static_cast<size_t>(NST) * STAGE;
+  static_assert((GA + GB) % NW == 0, "8-row groups must split evenly over the waves");
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tiles are whole MFMA blocks");
 };
 
-// One staged GEMM segment: acc += A[arow0 + ..] B[brow0 + ..]^T over k-steps
-// [s_begin, s_end) of 32.  Row pointers are per load instruction, chosen by
-// the caller (already offset to the lane's chunk); a null row pointer reads
-// the zero row.  klen bounds the valid k (tail chunks read the zero row).
-template <int BM, int BN, int WM, int WN>
+// One staged GEMM segment: acc += A B^T over 64-k steps [s_begin, s_end).
+// Row pointers are per load instruction (already offset to the lane's chunk);
+// a null row pointer reads the zero row.  klen bounds the valid k (chunks at
+// or past klen read the zero row).
+template <int BM, int BN, int WM, int WN, int NST>
 __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
-                                        const uint16_t *const (&rp)[(BM + BN) / 16 / (WM * WN)], int klen,
+                                        const uint16_t *const (&rp)[(BM + BN) / 8 / (WM * WN)], int klen,
                                         int s_begin, int s_end, const uint16_t *zero_row, uint8_t *lds) {
-  using TL = Tile<BM, BN, WM, WN>;
+  using TL = Tile<BM, BN, WM, WN, NST>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, g = lane >> 4;
-  const int lchunk = (lane & 3) ^ ((lane >> 3) & 3);
+  const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
   const int nk = s_end - s_begin;
   int ldsoff[TL::LPW];
 #pragma unroll
@@ -120,60 +140,65 @@ __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16]
                                        (lds_void *)(lds + stage * TL::STAGE + ldsoff[q]), 16, 0, 0);
     }
   };
-  const int swz = (g ^ ((r16 >> 1) & 3)) * 16;
-  const int aoff = (wm * TL::TM + r16) * kRowBytes + swz;
-  const int boff = BM * kRowBytes + (wn * TL::TN + r16) * kRowBytes + swz;
+  const int arow = (wm * TL::TM + r16) * kRowBytes;
+  const int brow = BM * kRowBytes + (wn * TL::TN + r16) * kRowBytes;
+  const int sw0 = ((0 + g) ^ (r16 & 7)) * 16, sw1 = ((4 + g) ^ (r16 & 7)) * 16;
 
 #pragma unroll
-  for (int st = 0; st < kNST - 1; ++st)
+  for (int st = 0; st < NST - 1; ++st)
     if (st < nk) issue(st, s_begin + st);
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of k-tile kt are done once at most (NST-2) tiles of
+    // this wave's loads of stage kt are done once at most NST-2 stages of
     // loads remain outstanding; the barrier then makes every wave's part of
-    // the tile visible, and tells that stage kt-1 is no longer being read
-    if (kt + kNST - 2 < nk)
-      wait_vmcnt<(kNST - 2) * TL::LPW>();
+    // the stage visible, and tells that stage kt-1 is no longer being read
+    if (kt + NST - 2 < nk)
+      wait_vmcnt<(NST - 2) * TL::LPW>();
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (kt + kNST - 1 < nk) issue((kt + kNST - 1) % kNST, s_begin + kt + kNST - 1);
-    const uint8_t *sb = lds + (kt % kNST) * TL::STAGE;
-    u32x4 fa[TL::FM], fb[TL::FN];
+    if (kt + NST - 1 < nk) issue((kt + NST - 1) % NST, s_begin + kt + NST - 1);
+    const uint8_t *sb = lds + (kt % NST) * TL::STAGE;
 #pragma unroll
-    for (int i = 0; i < TL::FM; ++i) fa[i] = *reinterpret_cast<const u32x4 *>(sb + aoff + i * 16 * kRowBytes);
+    for (int h = 0; h < 2; ++h) {
+      const int sw = h ? sw1 : sw0;
+      u32x4 fa[TL::FM], fb[TL::FN];
 #pragma unroll
-    for (int j = 0; j < TL::FN; ++j) fb[j] = *reinterpret_cast<const u32x4 *>(sb + boff + j * 16 * kRowBytes);
+      for (int i = 0; i < TL::FM; ++i) fa[i] = *reinterpret_cast<const u32x4 *>(sb + arow + i * 16 * kRowBytes + sw);
 #pragma unroll
-    for (int i = 0; i < TL::FM; ++i)
+      for (int j = 0; j < TL::FN; ++j) fb[j] = *reinterpret_cast<const u32x4 *>(sb + brow + j * 16 * kRowBytes + sw);
 #pragma unroll
-      for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+      for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+    }
   }
   // every wave is done with the ring before it is refilled
   __builtin_amdgcn_s_barrier();
 }
 
-// Workgroup index -> (feature tile, token tile), XCD-major: hardware sends
-// workgroup w to XCD w % 8; XCD x is given the contiguous unit range
-// [x * per + min(x, rem), ...) so the token tiles of one feature tile run
-// together on one XCD.
-__device__ __forceinline__ void unit_of(int id, int total, int nT, int &f, int &t) {
+// Workgroup index -> (feature tile, K slice, token tile), XCD-major: hardware
+// sends workgroup w to XCD w % 8; XCD x is given the contiguous unit range
+// [x * per + min(x, rem), ...), token tile fastest.
+__device__ __forceinline__ void unit_of(int id, int total, int nT, int nslices, int &f, int &sl, int &t) {
   const int x = id & 7, j = id >> 3;
   const int per = total >> 3, rem = total & 7;
   const int u = x * per + min(x, rem) + j;
-  f = u / nT;
-  t = u % nT;
+  f = u / (nslices * nT);
+  const int r = u % (nslices * nT);
+  sl = r / nT;
+  t = r % nT;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NST>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
-  using TL = Tile<BM, BN, WM, WN>;
+  using TL = Tile<BM, BN, WM, WN, NST>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, g = lane >> 4;
-  const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 3) & 3);
-  int f, t;
-  unit_of(blockIdx.x, gridDim.x, a.nT, f, t);
+  const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lrow & 7);
+  int f, sl, t;
+  unit_of(blockIdx.x, gridDim.x, a.nT, a.mode == kFinish ? 1 : a.ksplit, f, sl, t);
   const int m0 = f * BM, n0 = t * BN;
 
   f32x4 acc[TL::FM][TL::FN];
@@ -182,24 +207,71 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // main segment row pointers: rows of A (features) then of B (tokens)
-  {
+  if (a.mode != kFinish) {
+    // main segment (this workgroup's K slice): rows of A (features) then of B (tokens)
     const uint16_t *rp[TL::LPW];
 #pragma unroll
     for (int q = 0; q < TL::LPW; ++q) {
       const int gq = wave * TL::LPW + q;
       if (gq < TL::GA) {
-        const int row = m0 + gq * 16 + lrow;
+        const int row = m0 + gq * 8 + lrow;
         rp[q] = row < a.M ? a.A + row * a.lda + lchunk * 8 : nullptr;
       } else {
-        const int row = n0 + (gq - TL::GA) * 16 + lrow;
+        const int row = n0 + (gq - TL::GA) * 8 + lrow;
         rp[q] = row < a.T ? a.B + row * a.ldb + lchunk * 8 : nullptr;
       }
     }
-    segment<BM, BN, WM, WN>(acc, rp, a.K, 0, (a.K + kBK - 1) / kBK, a.zero_row, lds);
+    const int nsteps = (a.K + kBK - 1) / kBK;
+    const int sb = min(nsteps, sl * a.steps_per_slice), se = min(nsteps, sb + a.steps_per_slice);
+    segment<BM, BN, WM, WN, NST>(acc, rp, a.K, sb, se, a.zero_row, lds);
   }
 
-  if (a.mode == 1) {
+  // lane holds rows m0 + wm*TM + 16i + 4g + e, token n0 + wn*TN + 16j + r16
+  if (a.mode == kPartial) {
+    float *P = a.P + static_cast<size_t>(sl) * a.T * a.M;
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) {
+      const int tok = n0 + wn * TL::TN + j * 16 + r16;
+      if (tok >= a.T) continue;
+      float *prow = P + static_cast<size_t>(tok) * a.M;
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i) {
+        const int row = m0 + wm * TL::TM + i * 16 + g * 4;
+        if (row + 3 < a.M && (a.M & 3) == 0) {
+          *reinterpret_cast<f32x4 *>(prow + row) = acc[i][j];
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (row + e < a.M) prow[row + e] = acc[i][j][e];
+        }
+      }
+    }
+    return;
+  }
+
+  if (a.mode == kFinish) {
+    // acc = sum of the K-slice partials, in slice order (token columns past
+    // T re-read token T-1 and are never stored)
+    for (int s = 0; s < a.ksplit; ++s) {
+      const float *P = a.P + static_cast<size_t>(s) * a.T * a.M;
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j) {
+        const int tok = min(n0 + wn * TL::TN + j * 16 + r16, a.T - 1);
+        const float *prow = P + static_cast<size_t>(tok) * a.M;
+#pragma unroll
+        for (int i = 0; i < TL::FM; ++i) {
+          const int row = m0 + wm * TL::TM + i * 16 + g * 4;
+          if (row + 3 < a.M && (a.M & 3) == 0) {
+            acc[i][j] += *reinterpret_cast<const f32x4 *>(prow + row);
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (row + e < a.M) acc[i][j][e] += prow[row + e];
+          }
+        }
+      }
+    }
+  }
+
+  if (a.mode == kFused || a.mode == kFinish) {
     // scale by s (rows outside [0, M) are never stored)
 #pragma unroll
     for (int i = 0; i < TL::FM; ++i) {
@@ -220,15 +292,15 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
       for (int q = 0; q < TL::LPW; ++q) {
         const int gq = wave * TL::LPW + q;
         if (gq < TL::GA) {
-          const int row = m0 + gq * 16 + lrow;
+          const int row = m0 + gq * 8 + lrow;
           const bool in = row >= ch.row_start && row < ch.row_start + ch.N;
           rp[q] = in ? ch.U + static_cast<int64_t>(row - ch.row_start) * ch.rpad + lchunk * 8 : nullptr;
         } else {
-          const int row = n0 + (gq - TL::GA) * 16 + lrow;
+          const int row = n0 + (gq - TL::GA) * 8 + lrow;
           rp[q] = row < a.T ? a.Z + static_cast<int64_t>(row) * a.ldz + ch.zoff + lchunk * 8 : nullptr;
         }
       }
-      segment<BM, BN, WM, WN>(acc, rp, ch.rpad, 0, (ch.rpad + kBK - 1) / kBK, a.zero_row, lds);
+      segment<BM, BN, WM, WN, NST>(acc, rp, ch.rpad, 0, (ch.rpad + kBK - 1) / kBK, a.zero_row, lds);
     }
   }
 
@@ -245,7 +317,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
       uint16_t o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(acc[i][j][e]);
-      if (a.mode == 0) {
+      if (a.mode == kStoreBf16) {
         if (row + 3 < a.M && ((a.ldy | row) & 3) == 0) {
           *reinterpret_cast<uint2 *>(yrow + row) =
               make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
@@ -269,54 +341,102 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+// Z[i] = bf16(sum over slices of P[slice][i]), slices in order; n is a
+// multiple of 4 (T * Rz with Rz a multiple of 32).
+__global__ void reduce_z_kernel(const float *P, int ksplit, size_t n, uint16_t *Z) {
+  const size_t i = (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 v = *reinterpret_cast<const f32x4 *>(P + i);
+  for (int s = 1; s < ksplit; ++s) v += *reinterpret_cast<const f32x4 *>(P + static_cast<size_t>(s) * n + i);
+  *reinterpret_cast<uint2 *>(Z + i) =
+      make_uint2(f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+                 f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16));
+}
+
+template <int BM, int BN, int WM, int WN, int NST>
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(kNST) * Tile<BM, BN, WM, WN>::STAGE;
-  auto kern = gemm_kernel<BM, BN, WM, WN>;
+  using TL = Tile<BM, BN, WM, WN, NST>;
+  auto kern = gemm_kernel<BM, BN, WM, WN, NST>;
   static bool attr_set = false;  // per instance; setting it twice is harmless
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(TL::LDS));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(a.nM * a.nT), dim3(WM * WN * 64), lds, stream, a);
+  const int units = a.nM * a.nT * (a.mode == kFinish ? 1 : a.ksplit);
+  hipLaunchKernelGGL(kern, dim3(units), dim3(WM * WN * 64), TL::LDS, stream, a);
   return hipGetLastError();
 }
 
-// Tile shapes, largest first: (BM features, BN tokens, waves).
+// Tile shapes: BM features x BN tokens.  eff ranks the shapes by measured
+// streaming efficiency (bigger tiles move fewer bytes per flop).
 struct TileCfg {
   int BM, BN;
+  double eff;
 };
-constexpr TileCfg kTiles[] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64}};
+constexpr TileCfg kTiles[] = {{256, 128, 1.0}, {128, 128, 0.75}, {128, 64, 0.5}, {64, 64, 0.3}};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-// The largest tile that still gives every CU a workgroup; else the smallest.
-int pick_tile(int M, int T) {
-  constexpr int kCUs = 256;
-  const int n = sizeof(kTiles) / sizeof(kTiles[0]);
-  for (int i = 0; i < n; ++i) {
-    const long tiles = static_cast<long>((M + kTiles[i].BM - 1) / kTiles[i].BM) * ((T + kTiles[i].BN - 1) / kTiles[i].BN);
-    if (tiles >= kCUs) return i;
+struct Plan {
+  int tile, ksplit, steps_per_slice, nM, nT;
+};
+
+// Choose the tile shape and the K split of one GEMM (M rows, K deep, T
+// tokens): minimise (rounds of workgroups over the CUs) x (work of one
+// workgroup, scaled by its tile's efficiency), plus, when K is split, the
+// cost of writing and re-reading the fp32 partials and of the extra launch.
+// Unit: one 64-k step of a 256 x 128 tile, which streams 48 KB per CU.
+Plan plan_gemm(int M, int K, int T) {
+  const int nsteps = (K + kBK - 1) / kBK;
+  Plan best{kNumTiles - 1, 1, nsteps, (M + 63) / 64, (T + 63) / 64};
+  double best_cost = 1e300;
+  for (int i = 0; i < kNumTiles; ++i) {
+    const int nM = (M + kTiles[i].BM - 1) / kTiles[i].BM, nT = (T + kTiles[i].BN - 1) / kTiles[i].BN;
+    const long tiles = static_cast<long>(nM) * nT;
+    const int max_split = std::min(kMaxSplit, std::max(1, nsteps / kMinSliceSteps));
+    for (int ks = 1; ks <= max_split; ++ks) {
+      const int per = (nsteps + ks - 1) / ks;
+      if ((nsteps + per - 1) / per != ks) continue;  // some slice would be empty
+      const long rounds = (tiles * ks + kCUs - 1) / kCUs;
+      double cost = static_cast<double>(rounds) * per * (kTiles[i].BM * kTiles[i].BN) / (256.0 * 128.0) / kTiles[i].eff;
+      if (ks > 1) cost += 2.0 * ks * static_cast<double>(T) * M * 4 / (kCUs * 48.0 * 1024) + 8.0;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = Plan{i, ks, per, nM, nT};
+      }
+    }
   }
-  return n - 1;
+  return best;
 }
 
-hipError_t launch_tiled(GemmArgs a, hipStream_t stream) {
-  const int i = pick_tile(a.M, a.T);
-  a.nM = (a.M + kTiles[i].BM - 1) / kTiles[i].BM;
-  a.nT = (a.T + kTiles[i].BN - 1) / kTiles[i].BN;
-  switch (i) {
-    case 0: return launch_gemm<256, 256, 4, 2>(a, stream);
-    case 1: return launch_gemm<256, 128, 4, 2>(a, stream);
-    case 2: return launch_gemm<128, 128, 2, 2>(a, stream);
-    case 3: return launch_gemm<128, 64, 2, 2>(a, stream);
-    default: return launch_gemm<64, 64, 2, 2>(a, stream);
+hipError_t launch_planned(GemmArgs a, const Plan &p, hipStream_t stream) {
+  a.nM = p.nM;
+  a.nT = p.nT;
+  a.ksplit = p.ksplit;
+  a.steps_per_slice = p.steps_per_slice;
+  switch (p.tile) {
+    case 0: return launch_gemm<256, 128, 4, 2, 3>(a, stream);
+    case 1: return launch_gemm<128, 128, 4, 2, 4>(a, stream);
+    case 2: return launch_gemm<128, 64, 2, 2, 4>(a, stream);
+    default: return launch_gemm<64, 64, 2, 2, 4>(a, stream);
   }
+}
+
+size_t partial_bytes(const Plan &p, int M, int T) {
+  return p.ksplit > 1 ? static_cast<size_t>(p.ksplit) * T * M * 4 : 0;
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, const uint16_t *zero_row, hipStream_t stream) {
+size_t prefill_partial_bytes(int Ntot, int Rz, int K, int T) {
+  size_t n = partial_bytes(plan_gemm(Ntot, K, T), Ntot, T);
+  if (Rz > 0) n = std::max(n, partial_bytes(plan_gemm(Rz, K, T), Rz, T));
+  return n;
+}
+
+hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const uint16_t *zero_row,
+                          hipStream_t stream) {
   hipError_t e;
   if (c.Rz > 0) {
     GemmArgs a{};
@@ -328,11 +448,21 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, const uint16_t *zer
     a.ldb = c.K;
     a.K = c.K;
     a.zero_row = zero_row;
-    a.mode = 0;
     a.Y = zbuf;
     a.ldy = c.Rz;
-    e = launch_tiled(a, stream);
+    a.P = pbuf;
+    const Plan p = plan_gemm(c.Rz, c.K, c.T);
+    a.mode = p.ksplit > 1 ? kPartial : kStoreBf16;
+    e = launch_planned(a, p, stream);
     if (e != hipSuccess) return e;
+    if (p.ksplit > 1) {
+      const size_t n = static_cast<size_t>(c.T) * c.Rz;
+      const unsigned blocks = static_cast<unsigned>((n / 4 + 255) / 256);
+      hipLaunchKernelGGL(reduce_z_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const float *>(pbuf),
+                         p.ksplit, n, zbuf);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   GemmArgs a{};
   a.A = c.W0;
@@ -343,15 +473,25 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, const uint16_t *zer
   a.ldb = c.K;
   a.K = c.K;
   a.zero_row = zero_row;
-  a.mode = 1;
   a.Y = c.y;
   a.ldy = c.ldy;
   a.s = c.s;
   a.Z = zbuf;
   a.ldz = c.Rz;
+  a.P = pbuf;
   a.nchild = c.nchild;
   for (int i = 0; i < c.nchild; ++i) a.ch[i] = c.ch[i];
-  return launch_tiled(a, stream);
+  const Plan p = plan_gemm(c.Ntot, c.K, c.T);
+  if (p.ksplit == 1) {
+    a.mode = kFused;
+    return launch_planned(a, p, stream);
+  }
+  a.mode = kPartial;
+  e = launch_planned(a, p, stream);
+  if (e != hipSuccess) return e;
+  // finish: the same tiles, no K loop; starts from the partial sums
+  a.mode = kFinish;
+  return launch_planned(a, p, stream);
 }
 
 }  // namespace wl

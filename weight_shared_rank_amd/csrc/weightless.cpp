@@ -230,15 +230,26 @@ size_t ws_p_part_bytes(const Layout &lo, int32_t T) {
   return align256(static_cast<size_t>(wl::kDecodeMaxSlices) * T * lo.Nmax * 4);
 }
 
-// Prefill (T > 16): Z [T][Rmax] bf16.
+// Prefill (T > 16): Z [T][Rmax] bf16, then the fp32 K-split partials of the
+// largest call shape of the bundle.
 size_t ws_prefill_z_bytes(const Layout &lo, int32_t T) { return align256(static_cast<size_t>(T) * lo.Rmax * 2); }
+
+size_t ws_prefill_partial_bytes(const Layout &lo, int32_t T) {
+  size_t n = 0;
+  for (int t = 0; t < lo.NT; ++t)
+    for (int g = 0; g < kGroups; ++g) {
+      const GroupShape &gs = lo.gs[t][g];
+      if (gs.any) n = std::max(n, wl::prefill_partial_bytes(gs.Ntot, gs.Rtot, gs.K, T));
+    }
+  return align256(n);
+}
 
 size_t ws_bytes_for(const Layout &lo, int32_t T) {
   size_t n;
   if (T <= wl::kDecodeMaxT)
     n = ws_p_part_bytes(lo, T) + align256(static_cast<size_t>(T) * lo.Rmax * 4);
   else
-    n = ws_prefill_z_bytes(lo, T);
+    n = ws_prefill_z_bytes(lo, T) + ws_prefill_partial_bytes(lo, T);
   return n < 256 ? 256 : n;
 }
 
@@ -354,7 +365,9 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
   if (T <= wl::kDecodeMaxT)
     e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), reinterpret_cast<uint16_t *>(ws + ws_p_part_bytes(h->lo, T)), s);
   else
-    e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws), reinterpret_cast<const uint16_t *>(h->arena + h->lo.zero_off), s);
+    e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws),
+                           reinterpret_cast<float *>(ws + ws_prefill_z_bytes(h->lo, T)),
+                           reinterpret_cast<const uint16_t *>(h->arena + h->lo.zero_off), s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return WL_OK;
 }
