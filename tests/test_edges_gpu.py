@@ -188,3 +188,31 @@ def test_call_validation(gpu_lib):
     b0 = sdev.load(wl0, DEV)
     assert L.weightless_stacked_linear(b0.handle, 0, 0, *args()) == -4      # v absent, not tied
     assert L.weightless_linear(b0.handle, 0, 5, *args()) == -4              # up absent
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("T", [40, 200])
+def test_split_k_prefill(gpu_lib, T):
+    """Few-row GEMMs with long K take the K-split path (fp32 partials, a
+    delta slice, elementwise finish); stacked and single-family calls of one
+    group plan differently and must both fit the workspace and match the
+    oracle.  Row counts that are not multiples of 4 exercise the scalar
+    finish path; type 1 ties v to k."""
+    dims = {}
+    for t in (0, 1):
+        dims.update({(t, "q"): (4100, 4096), (t, "k"): (518, 4096), (t, "o"): (1000, 8192),
+                     (t, "gate"): (1024, 4096), (t, "up"): (1024, 4096), (t, "down"): (4096, 6144)})
+        if t == 0:
+            dims[(t, "v")] = (518, 4096)
+    wl = synth.custom(2, 1, 96, dims, layer_types=(0, 1), k_eq_v_types=(1,), cid=77)
+    ow = OracleWorkload(wl, DEV)
+    b = sdev.load(wl, DEV)
+    for layer in (0, 1):
+        for c in ("qkv", "o", "gate_up", "down", "q", "k", "v"):
+            x = wl.x(layer, c, T, DEV)
+            announce(f"split-K prefill T={T} layer {layer} {c}")
+            y = call(b, layer, c, x)
+            torch.cuda.synchronize()
+            ref_call = "k" if (c == "v" and wl.layer_types[layer] == 1) else c   # tied: v is k's output
+            res = compare(np64(y), ow.call(layer, ref_call, np64(x)))
+            assert res["ok"], f"layer {layer} {c}: {res}"

@@ -50,10 +50,11 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hip
 
 // Prefill path (T > 16): Z = X V into zbuf [T][Rz] (bf16), then the main
 // GEMM with the scale and rank-r epilogue.  GEMMs with few rows split K and
-// use pbuf for fp32 partials (prefill_partial_bytes bytes for this call
-// shape).  zero_row points at >= 16 zero bytes (used to mask rows and k
-// columns outside an operand).
-size_t prefill_partial_bytes(int Ntot, int Rz, int K, int T);
+// use pbuf for fp32 partials (prefill_partial_bytes bytes for a call of
+// Ntot rows, Rz total padded ranks, largest padded child rank rmax).
+// zero_row points at >= 16 zero bytes (used to mask rows and k columns
+// outside an operand).
+size_t prefill_partial_bytes(int Ntot, int Rz, int rmax, int K, int T);
 hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const uint16_t *zero_row,
                           hipStream_t stream);
 

@@ -34,11 +34,13 @@
 // with few rows (o, down, and Z = X V) split K into KS slices instead, so
 // that every CU streams.  Slices write fp32 partial tiles to the workspace;
 // a later launch sums them in slice order (deterministic): a reduce kernel
-// for Z, and for the main GEMM a "finish" launch of the same tiles that
-// starts from s (.) sum(P) and runs the delta.  Partials are combined across
-// launches, never across workgroups of one launch: that would need
-// device-scope release/acquire, which writes back / invalidates a whole L2
-// on this part.
+// for Z, and for the main GEMM an elementwise finish kernel.  A split main
+// GEMM gets one more slice per tile, which computes the delta Z U^T on its
+// own (it is another K range of the same product, with U and Z as the
+// operands); the finish kernel forms s (.) sum(main slices) + delta.
+// Partials are combined across launches, never across workgroups of one
+// launch: that would need device-scope release/acquire, which writes back /
+// invalidates a whole L2 on this part.
 //
 // Epilogue of the main GEMM: the fp32 accumulators are scaled by s per
 // feature row, then the same staged loop runs over the ranks of every child
@@ -70,8 +72,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 enum Mode : int32_t {
   kStoreBf16 = 0,  // Y = bf16(acc), [T][ldy]
   kFused = 1,      // Y = child map of bf16(s (.) acc + Z U^T)
-  kPartial = 2,    // P[slice][T][M] = acc (fp32)
-  kFinish = 3,     // Y = child map of bf16(s (.) sum_slices P + Z U^T)
+  kPartial = 2,    // P[slice][T][M] = acc (fp32); slice ksplit (if nchild) = Z U^T
 };
 
 struct GemmArgs {
@@ -93,7 +94,7 @@ struct GemmArgs {
   const float *s;
   const uint16_t *Z;  // [T][ldz]
   int32_t ldz;
-  float *P;           // partials [ksplit][T][M]
+  float *P;           // partials [ksplit (+1 for the delta)][T][M]
   int32_t nchild;
   ChildDesc ch[kMaxChildren];
 };
@@ -178,7 +179,7 @@ __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16]
 
 // Workgroup index -> (feature tile, K slice, token tile), XCD-major: hardware
 // sends workgroup w to XCD w % 8; XCD x is given the contiguous unit range
-// [x * per + min(x, rem), ...), token tile fastest.
+// [x * per + min(x, rem), ...) of the total units, token tile fastest.
 __device__ __forceinline__ void unit_of(int id, int total, int nT, int nslices, int &f, int &sl, int &t) {
   const int x = id & 7, j = id >> 3;
   const int per = total >> 3, rem = total & 7;
@@ -197,8 +198,19 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, g = lane >> 4;
   const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lrow & 7);
+  // units: the K slices of every tile first (XCD-major), then the delta
+  // slices (short; they run on the CUs that the K slices leave free or free up)
   int f, sl, t;
-  unit_of(blockIdx.x, gridDim.x, a.nT, a.mode == kFinish ? 1 : a.ksplit, f, sl, t);
+  const int nslices = a.mode == kPartial ? a.ksplit : 1;
+  const int main_units = a.nM * a.nT * nslices;
+  if (static_cast<int>(blockIdx.x) < main_units) {
+    unit_of(blockIdx.x, main_units, a.nT, nslices, f, sl, t);
+  } else {
+    const int u = blockIdx.x - main_units;
+    f = u / a.nT;
+    t = u % a.nT;
+    sl = a.ksplit;
+  }
   const int m0 = f * BM, n0 = t * BN;
 
   f32x4 acc[TL::FM][TL::FN];
@@ -207,7 +219,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (a.mode != kFinish) {
+  const bool delta_slice = a.mode == kPartial && sl == a.ksplit;
+  if (!delta_slice) {
     // main segment (this workgroup's K slice): rows of A (features) then of B (tokens)
     const uint16_t *rp[TL::LPW];
 #pragma unroll
@@ -224,6 +237,41 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
     const int nsteps = (a.K + kBK - 1) / kBK;
     const int sb = min(nsteps, sl * a.steps_per_slice), se = min(nsteps, sb + a.steps_per_slice);
     segment<BM, BN, WM, WN, NST>(acc, rp, a.K, sb, se, a.zero_row, lds);
+  }
+
+  if (a.mode == kFused) {
+    // scale by s (rows outside [0, M) are never stored)
+#pragma unroll
+    for (int i = 0; i < TL::FM; ++i) {
+      const int row = m0 + wm * TL::TM + i * 16 + g * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sc = row + e < a.M ? a.s[row + e] : 0.f;
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) acc[i][j][e] *= sc;
+      }
+    }
+  }
+  if (a.mode == kFused || delta_slice) {
+    // delta = Z U^T for every child with rows in this tile
+    for (int ci = 0; ci < a.nchild; ++ci) {
+      const ChildDesc &ch = a.ch[ci];
+      if (ch.rpad == 0 || m0 >= ch.row_start + ch.N || m0 + BM <= ch.row_start) continue;
+      const uint16_t *rp[TL::LPW];
+#pragma unroll
+      for (int q = 0; q < TL::LPW; ++q) {
+        const int gq = wave * TL::LPW + q;
+        if (gq < TL::GA) {
+          const int row = m0 + gq * 8 + lrow;
+          const bool in = row >= ch.row_start && row < ch.row_start + ch.N;
+          rp[q] = in ? ch.U + static_cast<int64_t>(row - ch.row_start) * ch.rpad + lchunk * 8 : nullptr;
+        } else {
+          const int row = n0 + (gq - TL::GA) * 8 + lrow;
+          rp[q] = row < a.T ? a.Z + static_cast<int64_t>(row) * a.ldz + ch.zoff + lchunk * 8 : nullptr;
+        }
+      }
+      segment<BM, BN, WM, WN, NST>(acc, rp, ch.rpad, 0, (ch.rpad + kBK - 1) / kBK, a.zero_row, lds);
+    }
   }
 
   // lane holds rows m0 + wm*TM + 16i + 4g + e, token n0 + wn*TN + 16j + r16
@@ -246,62 +294,6 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
       }
     }
     return;
-  }
-
-  if (a.mode == kFinish) {
-    // acc = sum of the K-slice partials, in slice order (token columns past
-    // T re-read token T-1 and are never stored)
-    for (int s = 0; s < a.ksplit; ++s) {
-      const float *P = a.P + static_cast<size_t>(s) * a.T * a.M;
-#pragma unroll
-      for (int j = 0; j < TL::FN; ++j) {
-        const int tok = min(n0 + wn * TL::TN + j * 16 + r16, a.T - 1);
-        const float *prow = P + static_cast<size_t>(tok) * a.M;
-#pragma unroll
-        for (int i = 0; i < TL::FM; ++i) {
-          const int row = m0 + wm * TL::TM + i * 16 + g * 4;
-          if (row + 3 < a.M && (a.M & 3) == 0) {
-            acc[i][j] += *reinterpret_cast<const f32x4 *>(prow + row);
-          } else {
-            for (int e = 0; e < 4; ++e)
-              if (row + e < a.M) acc[i][j][e] += prow[row + e];
-          }
-        }
-      }
-    }
-  }
-
-  if (a.mode == kFused || a.mode == kFinish) {
-    // scale by s (rows outside [0, M) are never stored)
-#pragma unroll
-    for (int i = 0; i < TL::FM; ++i) {
-      const int row = m0 + wm * TL::TM + i * 16 + g * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float sc = row + e < a.M ? a.s[row + e] : 0.f;
-#pragma unroll
-        for (int j = 0; j < TL::FN; ++j) acc[i][j][e] *= sc;
-      }
-    }
-    // delta = Z U^T for every child with rows in this tile
-    for (int ci = 0; ci < a.nchild; ++ci) {
-      const ChildDesc &ch = a.ch[ci];
-      if (ch.rpad == 0 || m0 >= ch.row_start + ch.N || m0 + BM <= ch.row_start) continue;
-      const uint16_t *rp[TL::LPW];
-#pragma unroll
-      for (int q = 0; q < TL::LPW; ++q) {
-        const int gq = wave * TL::LPW + q;
-        if (gq < TL::GA) {
-          const int row = m0 + gq * 8 + lrow;
-          const bool in = row >= ch.row_start && row < ch.row_start + ch.N;
-          rp[q] = in ? ch.U + static_cast<int64_t>(row - ch.row_start) * ch.rpad + lchunk * 8 : nullptr;
-        } else {
-          const int row = n0 + (gq - TL::GA) * 8 + lrow;
-          rp[q] = row < a.T ? a.Z + static_cast<int64_t>(row) * a.ldz + ch.zoff + lchunk * 8 : nullptr;
-        }
-      }
-      segment<BM, BN, WM, WN, NST>(acc, rp, ch.rpad, 0, (ch.rpad + kBK - 1) / kBK, a.zero_row, lds);
-    }
   }
 
   // store: lane holds rows m0 + wm*TM + 16i + 4g + e, token n0 + wn*TN + 16j + r16
@@ -353,6 +345,51 @@ __global__ void reduce_z_kernel(const float *P, int ksplit, size_t n, uint16_t *
                  f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16));
 }
 
+// y = bf16(s (.) sum_{slice < ksplit} P[slice] + P[ksplit] (the delta, if
+// any)) for one (token, 4 rows) per thread, stored through the child map.
+struct FinishArgs {
+  const float *P;
+  int32_t ksplit, has_delta, T, M;
+  const float *s;
+  uint16_t *Y;
+  int32_t ldy;
+  int32_t nchild;
+  ChildDesc ch[kMaxChildren];
+};
+
+__global__ void finish_kernel(FinishArgs a) {
+  const int groups = (a.M + 3) / 4;
+  const long id = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (id >= static_cast<long>(groups) * a.T) return;
+  const int tok = static_cast<int>(id / groups), row = static_cast<int>(id % groups) * 4;
+  const size_t plane = static_cast<size_t>(a.T) * a.M;
+  const float *p = a.P + static_cast<size_t>(tok) * a.M + row;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
+  if (row + 3 < a.M && (a.M & 3) == 0) {
+    for (int s = 0; s < a.ksplit; ++s) acc += *reinterpret_cast<const f32x4 *>(p + s * plane);
+    if (a.has_delta) d = *reinterpret_cast<const f32x4 *>(p + a.ksplit * plane);
+    sc = *reinterpret_cast<const f32x4 *>(a.s + row);
+  } else {
+    for (int e = 0; e < 4 && row + e < a.M; ++e) {
+      for (int s = 0; s < a.ksplit; ++s) acc[e] += p[s * plane + e];
+      if (a.has_delta) d[e] = p[a.ksplit * plane + e];
+      sc[e] = a.s[row + e];
+    }
+  }
+  uint16_t *yrow = a.Y + static_cast<size_t>(tok) * a.ldy;
+  for (int e = 0; e < 4; ++e) {
+    const int r = row + e;
+    if (r >= a.M) break;
+    int ci = 0;
+    while (ci + 1 < a.nchild && r >= a.ch[ci + 1].row_start) ++ci;
+    const ChildDesc &ch = a.ch[ci];
+    const uint16_t o = f32_to_bf16(sc[e] * acc[e] + d[e]);
+    const int jj = r - ch.row_start;
+    yrow[ch.y_off + jj] = o;
+    if (ch.dup_off >= 0) yrow[ch.dup_off + jj] = o;
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int NST>
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
   using TL = Tile<BM, BN, WM, WN, NST>;
@@ -364,7 +401,7 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int units = a.nM * a.nT * (a.mode == kFinish ? 1 : a.ksplit);
+  const int units = a.nM * a.nT * (a.mode == kPartial ? a.ksplit + (a.nchild > 0 ? 1 : 0) : 1);
   hipLaunchKernelGGL(kern, dim3(units), dim3(WM * WN * 64), TL::LDS, stream, a);
   return hipGetLastError();
 }
@@ -383,24 +420,34 @@ struct Plan {
 };
 
 // Choose the tile shape and the K split of one GEMM (M rows, K deep, T
-// tokens): minimise (rounds of workgroups over the CUs) x (work of one
-// workgroup, scaled by its tile's efficiency), plus, when K is split, the
-// cost of writing and re-reading the fp32 partials and of the extra launch.
-// Unit: one 64-k step of a 256 x 128 tile, which streams 48 KB per CU.
-Plan plan_gemm(int M, int K, int T) {
+// tokens, plus dsteps 64-k steps of rank-r delta per tile): minimise the
+// estimated makespan -- rounds of workgroups over the CUs times the work of
+// one workgroup, scaled by the tile's efficiency -- plus, when K is split, the
+// cost of writing and re-reading the fp32 partials and of the finish launch.
+// A split GEMM runs the delta as one short extra slice per tile, which fills
+// in behind the K slices.  Unit: one 64-k step of a 256 x 128 tile (48 KB
+// streamed per CU).
+Plan plan_gemm(int M, int K, int T, int dsteps) {
   const int nsteps = (K + kBK - 1) / kBK;
   Plan best{kNumTiles - 1, 1, nsteps, (M + 63) / 64, (T + 63) / 64};
   double best_cost = 1e300;
   for (int i = 0; i < kNumTiles; ++i) {
     const int nM = (M + kTiles[i].BM - 1) / kTiles[i].BM, nT = (T + kTiles[i].BN - 1) / kTiles[i].BN;
     const long tiles = static_cast<long>(nM) * nT;
+    const double scale = (kTiles[i].BM * kTiles[i].BN) / (256.0 * 128.0) / kTiles[i].eff;
     const int max_split = std::min(kMaxSplit, std::max(1, nsteps / kMinSliceSteps));
     for (int ks = 1; ks <= max_split; ++ks) {
       const int per = (nsteps + ks - 1) / ks;
       if ((nsteps + per - 1) / per != ks) continue;  // some slice would be empty
       const long rounds = (tiles * ks + kCUs - 1) / kCUs;
-      double cost = static_cast<double>(rounds) * per * (kTiles[i].BM * kTiles[i].BN) / (256.0 * 128.0) / kTiles[i].eff;
-      if (ks > 1) cost += 2.0 * ks * static_cast<double>(T) * M * 4 / (kCUs * 48.0 * 1024) + 8.0;
+      double cost;
+      if (ks == 1) {
+        cost = static_cast<double>(rounds) * (per + dsteps) * scale;
+      } else {
+        const double total = static_cast<double>(tiles) * (static_cast<double>(ks) * per + dsteps) / kCUs;
+        cost = std::max(static_cast<double>(rounds) * per, total) * scale;
+        cost += 2.0 * (ks + (dsteps > 0 ? 1 : 0)) * static_cast<double>(T) * M * 4 / (kCUs * 48.0 * 1024) + 8.0;
+      }
       if (cost < best_cost) {
         best_cost = cost;
         best = Plan{i, ks, per, nM, nT};
@@ -408,6 +455,12 @@ Plan plan_gemm(int M, int K, int T) {
     }
   }
   return best;
+}
+
+int delta_steps(const CallDesc &c) {
+  int r = 0;
+  for (int i = 0; i < c.nchild; ++i) r = std::max(r, static_cast<int>(c.ch[i].rpad));
+  return (r + kBK - 1) / kBK;
 }
 
 hipError_t launch_planned(GemmArgs a, const Plan &p, hipStream_t stream) {
@@ -423,15 +476,16 @@ hipError_t launch_planned(GemmArgs a, const Plan &p, hipStream_t stream) {
   }
 }
 
-size_t partial_bytes(const Plan &p, int M, int T) {
-  return p.ksplit > 1 ? static_cast<size_t>(p.ksplit) * T * M * 4 : 0;
+size_t partial_bytes(const Plan &p, int M, int T, bool delta) {
+  return p.ksplit > 1 ? static_cast<size_t>(p.ksplit + (delta ? 1 : 0)) * T * M * 4 : 0;
 }
 
 }  // namespace
 
-size_t prefill_partial_bytes(int Ntot, int Rz, int K, int T) {
-  size_t n = partial_bytes(plan_gemm(Ntot, K, T), Ntot, T);
-  if (Rz > 0) n = std::max(n, partial_bytes(plan_gemm(Rz, K, T), Rz, T));
+size_t prefill_partial_bytes(int Ntot, int Rz, int rmax, int K, int T) {
+  const int dsteps = (rmax + kBK - 1) / kBK;
+  size_t n = partial_bytes(plan_gemm(Ntot, K, T, dsteps), Ntot, T, dsteps > 0);
+  if (Rz > 0) n = std::max(n, partial_bytes(plan_gemm(Rz, K, T, 0), Rz, T, false));
   return n;
 }
 
@@ -451,7 +505,7 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const 
     a.Y = zbuf;
     a.ldy = c.Rz;
     a.P = pbuf;
-    const Plan p = plan_gemm(c.Rz, c.K, c.T);
+    const Plan p = plan_gemm(c.Rz, c.K, c.T, 0);
     a.mode = p.ksplit > 1 ? kPartial : kStoreBf16;
     e = launch_planned(a, p, stream);
     if (e != hipSuccess) return e;
@@ -481,17 +535,31 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const 
   a.P = pbuf;
   a.nchild = c.nchild;
   for (int i = 0; i < c.nchild; ++i) a.ch[i] = c.ch[i];
-  const Plan p = plan_gemm(c.Ntot, c.K, c.T);
+  const Plan p = plan_gemm(c.Ntot, c.K, c.T, delta_steps(c));
   if (p.ksplit == 1) {
     a.mode = kFused;
     return launch_planned(a, p, stream);
   }
+  // K slices plus (if any child has a rank) one delta slice per tile
+  const bool any_rank = delta_steps(c) > 0;
+  if (!any_rank) a.nchild = 0;
   a.mode = kPartial;
   e = launch_planned(a, p, stream);
   if (e != hipSuccess) return e;
-  // finish: the same tiles, no K loop; starts from the partial sums
-  a.mode = kFinish;
-  return launch_planned(a, p, stream);
+  FinishArgs fa{};
+  fa.P = pbuf;
+  fa.ksplit = p.ksplit;
+  fa.has_delta = any_rank ? 1 : 0;
+  fa.T = c.T;
+  fa.M = c.Ntot;
+  fa.s = c.s;
+  fa.Y = c.y;
+  fa.ldy = c.ldy;
+  fa.nchild = c.nchild;
+  for (int i = 0; i < c.nchild; ++i) fa.ch[i] = c.ch[i];
+  const long threads = static_cast<long>((c.Ntot + 3) / 4) * c.T;
+  hipLaunchKernelGGL(finish_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream, fa);
+  return hipGetLastError();
 }
 
 }  // namespace wl

@@ -239,7 +239,14 @@ size_t ws_prefill_partial_bytes(const Layout &lo, int32_t T) {
   for (int t = 0; t < lo.NT; ++t)
     for (int g = 0; g < kGroups; ++g) {
       const GroupShape &gs = lo.gs[t][g];
-      if (gs.any) n = std::max(n, wl::prefill_partial_bytes(gs.Ntot, gs.Rtot, gs.K, T));
+      if (!gs.any) continue;
+      // the stacked call and every single-family call of the group
+      int rmax = 0;
+      for (int c = 0; c < gs.nchild; ++c) {
+        rmax = std::max(rmax, gs.rpad[c]);
+        n = std::max(n, wl::prefill_partial_bytes(gs.N[c], gs.rpad[c], gs.rpad[c], gs.K, T));
+      }
+      n = std::max(n, wl::prefill_partial_bytes(gs.Ntot, gs.Rtot, rmax, gs.K, T));
     }
   return align256(n);
 }
@@ -364,10 +371,17 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
   hipError_t e;
   if (T <= wl::kDecodeMaxT)
     e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), reinterpret_cast<uint16_t *>(ws + ws_p_part_bytes(h->lo, T)), s);
-  else
+  else {
+    // internal guard: this call's split partials fit the region sized for
+    // the largest call shape of the bundle
+    int rmax = 0;
+    for (int c = 0; c < rv.c.nchild; ++c) rmax = std::max(rmax, static_cast<int>(rv.c.ch[c].rpad));
+    if (wl::prefill_partial_bytes(rv.c.Ntot, rv.c.Rz, rmax, rv.c.K, T) > ws_prefill_partial_bytes(h->lo, T))
+      return fail(WL_ENOSPACE, "internal: prefill partials of this call exceed the planned workspace");
     e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws),
                            reinterpret_cast<float *>(ws + ws_prefill_z_bytes(h->lo, T)),
                            reinterpret_cast<const uint16_t *>(h->arena + h->lo.zero_off), s);
+  }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return WL_OK;
 }
