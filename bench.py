@@ -370,9 +370,10 @@ def main():
     ap.add_argument("--band-reuse", action="store_true",
                     help="report whether a band-shared W0 re-read by the next layer is served from the 256 MB "
                          "Infinity Cache or from HBM (prints one JSON line)")
-    ap.add_argument("--profile", action="store_true",
-                    help="for rocprofv3 counter runs: one eager decode step of the headline workload, then a "
-                         "plain 1 GiB device copy whose counters calibrate FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--profile", choices=["decode", "prefill"],
+                    help="for rocprofv3 counter runs: one eager step (decode: the headline workload at T=1; "
+                         "prefill: the Gemma-4-31B mixed prefill at T=512), then a plain 1 GiB device copy whose "
+                         "counters calibrate FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the weightless linear here runs on a single MI355X "
@@ -390,15 +391,18 @@ def main():
     wl4 = synth.workload(4)
     if args.profile:
         import synth.device as sdev
-        bundle = sdev.load(wl4, dev)
-        step = Step(wl4, bundle, 1, CALLS, dev)
+        wlp, T = (wl4, 1) if args.profile == "decode" else (synth.workload(5), 512)
+        bundle = sdev.load(wlp, dev)
+        step = Step(wlp, bundle, T, CALLS, dev)
+        torch.cuda.synchronize()
         step.run()
         torch.cuda.synchronize()
         src = torch.ones(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"profile": "done", "bytes_per_call": step.bytes_rd / len(step.items),
+        print(json.dumps({"profile": args.profile, "bytes_per_call": step.bytes_rd / len(step.items),
+                          "flops_per_call": step.flops / len(step.items),
                           "calls": len(step.items), "copy_bytes": src.numel() * 2}), flush=True)
         return
 
@@ -451,8 +455,9 @@ def main():
                            "workload": "gemma4-31b mixed prefill: 10 full + 50 sliding layers, G=1 per type, "
                                        "rank 1024, T=512, graph-replayed step",
                            "roofline": {"bound": "mfma",
-                                        "kernel": "gemm_kernel (Z = X V, then the main GEMM with the fused s and "
-                                                  "U z epilogue: two launches per call)",
+                                        "kernel": "gemm_kernel (Z = X V, then the main GEMM with the s and U z "
+                                                  "epilogue; GEMMs with few rows split K, adding reduce_z_kernel / "
+                                                  "finish_kernel: 2-4 launches per call)",
                                         "achieved": round(p["call_TFLOPs"], 2), "peak": BF16_PEAK_TFLOPS,
                                         "unit": "TFLOP/s", "frac": round(p["call_TFLOPs"] / BF16_PEAK_TFLOPS, 4),
                                         "flops_per_call": p["flops_per_call"], "avg_call_us": round(p["avg_call_us"], 2),
