@@ -134,17 +134,18 @@ wl_status theta_bundle_free(wl_bundle *bundle);
 /* Workspace bytes needed by any weightless_linear / weightless_stacked_linear
  * call on this bundle with T tokens (T <= 16: decode path; T > 16: prefill
  * path).  The workspace holds intermediate results of one call (fp32 K-slice
- * partials for decode, Z = X V for prefill); it needs no initialization and
- * keeps nothing between calls.
+ * partials and z for decode; Z = X V and fp32 K-slice partials for prefill);
+ * it needs no initialization and keeps nothing between calls.
  * 0 with wl_last_error() set on error. */
 size_t weightless_workspace_bytes(const wl_bundle *bundle, int32_t T);
 
 /* y = s (.) (W0 x) + U (V^T x) for one family of one layer.
  *  d_x bf16 [T, K], d_y bf16 [T, N] (must not alias d_x), T >= 0 (T = 0: no-op).
- *  T <= 16 runs the decode path (two launches: the K-slice partials of
- *  z = V^T x, then the W0 stream with the fused scale and U z epilogue),
- *  T > 16 the prefill MFMA GEMMs (two launches: Z = X V, then
- *  Y = (X W0^T) (.) s + Z U^T).
+ *  T <= 16 runs the decode path (two launches: one streams [W0; V^T] x into
+ *  fp32 K-slice partials of W0 x and z = V^T x, the other sums them, scales
+ *  by s, adds U z and stores y), T > 16 the prefill MFMA GEMMs (Z = X V,
+ *  then Y = (X W0^T) (.) s + Z U^T; GEMMs with few rows split K and add a
+ *  summing launch: 2 to 4 launches).
  *  family WL_V on a K=V-tied layer type evaluates k's bundle.
  *  d_ws: workspace of at least weightless_workspace_bytes(bundle, T) bytes,
  *  256-byte aligned; concurrent calls need distinct workspaces. */
