@@ -161,6 +161,22 @@ wl_status weightless_stacked_linear(const wl_bundle *bundle, int32_t layer, int3
                                     const void *d_x, int32_t T, void *d_y,
                                     void *d_ws, size_t ws_bytes, void *stream);
 
+/* Workspace bytes weightless_materialize needs for any family of this bundle
+ * (the V rows of one family, K x padded rank bf16); 0 on error. */
+size_t weightless_materialize_workspace_bytes(const wl_bundle *bundle);
+
+/* The dense weight a bundle stands for: W_eff = diag(s) W0 + U V^T of one
+ * family of one layer ("Override the graph build" page: the variant that
+ * precomputes the effective weight outside the graph), written as bf16
+ * [N, K] row-major to d_weff (16-byte aligned, must not overlap the arena).
+ * Each element is one fp32 sum s_i W0[i][j] + sum_k U[i][k] V[j][k] rounded
+ * to bf16 (nearest even).  family WL_V on a K=V-tied layer type gives k's
+ * weight.  d_ws: at least weightless_materialize_workspace_bytes(bundle)
+ * bytes, 256-byte aligned.  Two launches on `stream` (V^T -> V rows, then an
+ * MFMA GEMM over the ranks with s W0 added in its epilogue). */
+wl_status weightless_materialize(const wl_bundle *bundle, int32_t layer, int32_t family, void *d_weff,
+                                 void *d_ws, size_t ws_bytes, void *stream);
+
 /* Output width N of a single-family call, or of a stacked call (stack >= 0
  * with family < 0); 0 on error.  Host-only. */
 int32_t weightless_out_dim(const wl_bundle *bundle, int32_t layer, int32_t family, int32_t stack);

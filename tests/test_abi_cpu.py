@@ -193,3 +193,5 @@ def test_empty_bundle_and_null_handles(L):
     assert L.weightless_stacked_linear(None, 0, 0, FAKE_ARENA, 1, FAKE_ARENA, FAKE_ARENA, 1, None) == -1
     assert L.weightless_workspace_bytes(None, 1) == 0
     assert L.weightless_out_dim(None, 0, 0, -1) == 0
+    assert L.weightless_materialize_workspace_bytes(None) == 0
+    assert L.weightless_materialize(None, 0, 0, FAKE_ARENA, FAKE_ARENA, 1 << 20, None) == -1

@@ -28,7 +28,8 @@ DECODE_MAX_T = 16
 # every symbol include/weightless.h declares
 EXPORTS = ("theta_bundle_arena_bytes", "theta_bundle_load", "theta_bundle_free",
            "weightless_workspace_bytes",
-           "weightless_linear", "weightless_stacked_linear", "weightless_out_dim", "wl_last_error")
+           "weightless_linear", "weightless_stacked_linear", "weightless_out_dim", "wl_last_error",
+           "weightless_materialize_workspace_bytes", "weightless_materialize")
 
 
 class WlBundleSpec(ctypes.Structure):
@@ -72,6 +73,8 @@ def lib():
         "weightless_stacked_linear": (i32, [vp, i32, i32, vp, i32, vp, vp, sz, vp]),
         "weightless_out_dim": (i32, [vp, i32, i32, i32]),
         "wl_last_error": (ctypes.c_char_p, []),
+        "weightless_materialize_workspace_bytes": (sz, [vp]),
+        "weightless_materialize": (i32, [vp, i32, i32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -219,3 +222,26 @@ class ThetaBundle:
         """The stacked q|k|v or gate|up call over one x."""
         return self._call(lib().weightless_stacked_linear, layer, STACKS[stack], x, y, ws, stream,
                           self.out_dim(layer, stack=stack))
+
+    def in_dim(self, layer: int, family: str) -> int:
+        """K of one family of one layer (from the spec)."""
+        t = self.spec.layer_type[layer] if self.spec.layer_type else 0
+        f = FAMILY[family]
+        if family == "v" and (self.spec.k_eq_v_type_mask >> t) & 1:
+            f = FAMILY["k"]
+        return self.spec.in_dim[t][f]
+
+    def materialize(self, layer: int, family: str, out=None, ws=None, stream=None):
+        """W_eff = diag(s) W0 + U V^T of one family, bf16 [N, K] on the device."""
+        import torch
+        n, k = self.out_dim(layer, family=family), self.in_dim(layer, family)
+        if out is None:
+            out = torch.empty((n, k), dtype=torch.bfloat16, device=self.arena.device)
+        if ws is None:
+            need = lib().weightless_materialize_workspace_bytes(self.handle)
+            if need == 0:
+                raise WlError(-1, last_error())
+            ws = torch.empty(need, dtype=torch.uint8, device=self.arena.device)
+        _check(lib().weightless_materialize(self.handle, layer, FAMILY[family], out.data_ptr(), ws.data_ptr(),
+                                            ws.numel(), _stream_ptr(stream)))
+        return out

@@ -58,6 +58,12 @@ size_t prefill_partial_bytes(int Ntot, int Rz, int rmax, int K, int T);
 hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const uint16_t *zero_row,
                           hipStream_t stream);
 
+// Effective weight: out[N][K] (bf16) = s (.) W0 + U V^T, with V given as
+// rows [K][rpad] (ranks contiguous) and U as [N][rpad]; rpad may be 0.
+hipError_t launch_materialize(const uint16_t *V, const uint16_t *U, int32_t N, int32_t K, int32_t rpad,
+                              const float *s, const uint16_t *W0, uint16_t *out, const uint16_t *zero_row,
+                              hipStream_t stream);
+
 // Load-time helpers.
 hipError_t launch_fill_zero(void *dst, size_t bytes, hipStream_t stream);
 // V [K, r] (row-major, bf16) -> V^T rows [r, K] at dst (row stride K).

@@ -73,6 +73,7 @@ enum Mode : int32_t {
   kStoreBf16 = 0,  // Y = bf16(acc), [T][ldy]
   kFused = 1,      // Y = child map of bf16(s (.) acc + Z U^T)
   kPartial = 2,    // P[slice][T][M] = acc (fp32); slice ksplit (if nchild) = Z U^T
+  kAddScaled = 3,  // Y = bf16(acc + s[t] * W[t][m]), [T][ldy] (effective-weight materialization)
 };
 
 struct GemmArgs {
@@ -95,6 +96,8 @@ struct GemmArgs {
   const uint16_t *Z;  // [T][ldz]
   int32_t ldz;
   float *P;           // partials [ksplit (+1 for the delta)][T][M]
+  const uint16_t *W;  // kAddScaled: [T][ldw] bf16, scaled by s[t] and added
+  int64_t ldw;
   int32_t nchild;
   ChildDesc ch[kMaxChildren];
 };
@@ -309,7 +312,16 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
       uint16_t o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(acc[i][j][e]);
-      if (a.mode == kStoreBf16) {
+      if (a.mode == kAddScaled) {
+        // here the B rows ("tokens") are the rows of the weight and the A rows
+        // its columns: y[t][m] = acc + s[t] * W[t][m]
+        const float sc = a.s[tok];
+        const uint16_t *wrow = a.W + static_cast<int64_t>(tok) * a.ldw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (row + e < a.M) o[e] = f32_to_bf16(acc[i][j][e] + sc * bf16_to_f32(wrow[row + e]));
+      }
+      if (a.mode == kStoreBf16 || a.mode == kAddScaled) {
         if (row + 3 < a.M && ((a.ldy | row) & 3) == 0) {
           *reinterpret_cast<uint2 *>(yrow + row) =
               make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
@@ -427,7 +439,7 @@ struct Plan {
 // A split GEMM runs the delta as one short extra slice per tile, which fills
 // in behind the K slices.  Unit: one 64-k step of a 256 x 128 tile (48 KB
 // streamed per CU).
-Plan plan_gemm(int M, int K, int T, int dsteps) {
+Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true) {
   const int nsteps = (K + kBK - 1) / kBK;
   Plan best{kNumTiles - 1, 1, nsteps, (M + 63) / 64, (T + 63) / 64};
   double best_cost = 1e300;
@@ -435,10 +447,10 @@ Plan plan_gemm(int M, int K, int T, int dsteps) {
     const int nM = (M + kTiles[i].BM - 1) / kTiles[i].BM, nT = (T + kTiles[i].BN - 1) / kTiles[i].BN;
     const long tiles = static_cast<long>(nM) * nT;
     const double scale = (kTiles[i].BM * kTiles[i].BN) / (256.0 * 128.0) / kTiles[i].eff;
-    const int max_split = std::min(kMaxSplit, std::max(1, nsteps / kMinSliceSteps));
+    const int max_split = allow_split ? std::min(kMaxSplit, std::max(1, nsteps / kMinSliceSteps)) : 1;
     for (int ks = 1; ks <= max_split; ++ks) {
       const int per = (nsteps + ks - 1) / ks;
-      if ((nsteps + per - 1) / per != ks) continue;  // some slice would be empty
+      if (nsteps > 0 && (nsteps + per - 1) / per != ks) continue;  // some slice would be empty
       const long rounds = (tiles * ks + kCUs - 1) / kCUs;
       double cost;
       if (ks == 1) {
@@ -560,6 +572,29 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const 
   const long threads = static_cast<long>((c.Ntot + 3) / 4) * c.T;
   hipLaunchKernelGGL(finish_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream, fa);
   return hipGetLastError();
+}
+
+hipError_t launch_materialize(const uint16_t *V, const uint16_t *U, int32_t N, int32_t K, int32_t rpad,
+                              const float *s, const uint16_t *W0, uint16_t *out, const uint16_t *zero_row,
+                              hipStream_t stream) {
+  // out[i][j] = s[i] W0[i][j] + sum_k U[i][k] V[j][k]: A = V rows (the K
+  // columns of W_eff), B = U rows (its N rows), reduction over the ranks
+  GemmArgs a{};
+  a.A = V;
+  a.M = K;
+  a.lda = rpad;
+  a.B = U;
+  a.T = N;
+  a.ldb = rpad;
+  a.K = rpad;
+  a.zero_row = zero_row;
+  a.mode = kAddScaled;
+  a.Y = out;
+  a.ldy = K;
+  a.s = s;
+  a.W = W0;
+  a.ldw = K;
+  return launch_planned(a, plan_gemm(K, rpad, N, 0, false), stream);
 }
 
 }  // namespace wl

@@ -549,6 +549,49 @@ wl_status weightless_stacked_linear(const wl_bundle *bundle, int32_t layer, int3
   return run_call(bundle, layer, -1, stack, d_x, T, d_y, d_ws, ws_bytes, stream);
 }
 
+size_t weightless_materialize_workspace_bytes(const wl_bundle *bundle) {
+  if (!bundle) {
+    fail(WL_EINVAL, "bundle is NULL");
+    return 0;
+  }
+  size_t n = 256;
+  const Layout &lo = bundle->lo;
+  for (int t = 0; t < lo.NT; ++t)
+    for (int g = 0; g < kGroups; ++g) {
+      const GroupShape &gs = lo.gs[t][g];
+      for (int c = 0; c < gs.nchild; ++c)
+        n = std::max(n, align256(static_cast<size_t>(gs.K) * gs.rpad[c] * 2));
+    }
+  return n;
+}
+
+wl_status weightless_materialize(const wl_bundle *bundle, int32_t layer, int32_t family, void *d_weff, void *d_ws,
+                                 size_t ws_bytes, void *stream) {
+  Resolved rv;
+  wl_status st = resolve(bundle, layer, family, -1, rv);
+  if (st != WL_OK) return st;
+  if (!d_weff || !d_ws) return fail(WL_EINVAL, "w_eff and workspace must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(d_weff) % 16) return fail(WL_EINVAL, "w_eff must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(d_ws) % 256) return fail(WL_EINVAL, "workspace must be 256-byte aligned");
+  const size_t need = weightless_materialize_workspace_bytes(bundle);
+  if (ws_bytes < need) return fail(WL_ENOSPACE, "workspace has %zu bytes, materialize needs %zu", ws_bytes, need);
+  const wl::CallDesc &c = rv.c;
+  const wl::ChildDesc &ch = c.ch[0];
+  const uint8_t *wb = static_cast<const uint8_t *>(d_weff);
+  const size_t wbytes = static_cast<size_t>(c.Ntot) * c.K * 2;
+  if (wb < bundle->arena + bundle->arena_bytes && bundle->arena < wb + wbytes)
+    return fail(WL_EINVAL, "w_eff must not overlap the bundle arena");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t *vrows = static_cast<uint16_t *>(d_ws);
+  // V^T [rpad][K] -> V rows [K][rpad] (ranks contiguous), the GEMM's A operand
+  hipError_t e = wl::launch_transpose_v(c.Vt, ch.rpad, c.K, vrows, s);
+  if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  e = wl::launch_materialize(vrows, ch.U, c.Ntot, c.K, ch.rpad, c.s, c.W0, static_cast<uint16_t *>(d_weff),
+                             reinterpret_cast<const uint16_t *>(bundle->arena + bundle->lo.zero_off), s);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return WL_OK;
+}
+
 int32_t weightless_out_dim(const wl_bundle *bundle, int32_t layer, int32_t family, int32_t stack) {
   Resolved rv;
   if (resolve(bundle, layer, stack >= 0 ? -1 : family, stack >= 0 ? stack : -1, rv) != WL_OK) return 0;
