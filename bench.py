@@ -69,16 +69,17 @@ def call_flops(wl, layer, fams, T):
 
 
 class Step:
-    """Every call of every layer, with preallocated inputs and outputs."""
+    """Every call of every layer (or of the given layers), with preallocated
+    inputs and outputs."""
 
-    def __init__(self, wl, bundle, T, calls, dev):
+    def __init__(self, wl, bundle, T, calls, dev, layers=None):
         import torch
         self.items = []
         self.bytes_rd = 0
         self.bytes_wr = 0
         self.flops = 0
         self.per_call = {}
-        for layer in range(wl.num_layers):
+        for layer in (range(wl.num_layers) if layers is None else layers):
             for name, fams in calls:
                 lt = wl.layer_types[layer]
                 fams_here = [f for f in fams if (lt, f) in wl.dims or (f == "v" and lt in wl.k_eq_v_types)]
@@ -232,6 +233,80 @@ def prefill_section(wl, T, calls, steps, warmup, dev, reps=1):
     return out
 
 
+def dense_comparison(wl, T, nlayers, steps, warmup, dev):
+    """The weightless step against the dense weight it stands for, on the
+    first nlayers layers (one band of the headline workload).  W_eff =
+    diag(s) W0 + U V^T of every family is materialized by the library; the
+    dense step then runs (a) the same decode kernels on a rank-0 bundle whose
+    per-layer W0 is W_eff and s = 1, and (b) torch.matmul (hipBLASLt) on the
+    same W_eff, as another system's reference.  Same x, same call order."""
+    import torch
+    import synth
+    import synth.device as sdev
+    layers = list(range(nlayers))
+    bundle = sdev.load(wl, dev)
+    wstep = Step(wl, bundle, T, CALLS, dev, layers=layers)
+    t_w, g = time_graph(wstep, steps, warmup)
+    del g
+    # materialize every family of every layer
+    weff = {}
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mat_bytes = 0
+    e0.record()
+    for l in layers:
+        for f in synth.FAMILIES:
+            if (0, f) in wl.dims:
+                weff[(l, f)] = bundle.materialize(l, f)
+                mat_bytes += weff[(l, f)].numel() * 2
+    e1.record()
+    torch.cuda.synchronize()
+    t_mat = e0.elapsed_time(e1) * 1e-3
+    dims = {k: v for k, v in wl.dims.items() if k[0] == 0}
+    dwl = synth.custom(nlayers, nlayers, 0, dims, cid=wl.cid)
+
+    def tensors(kind, index, ltype, fam):
+        if kind == "w0":
+            return weff[(index, fam)]
+        return torch.ones(wl.shape(0, fam)[0], dtype=torch.float32, device=dev)
+    dense = sdev.load(dwl, dev, tensors=tensors)
+    dstep = Step(dwl, dense, T, CALLS, dev)
+    # same activations as the weightless step
+    for (l, n, st, x, y), (l2, n2, st2, x2, y2) in zip(wstep.items, dstep.items):
+        x2.copy_(x)
+    t_d, g = time_graph(dstep, steps, warmup)
+    del g
+    dense_bytes = sum(weff[k].numel() * 2 for k in weff)
+    # torch.matmul on the concatenated dense weights of each call
+    wcat = {}
+    for l in layers:
+        for name, fams in CALLS:
+            wcat[(l, name)] = torch.cat([weff[(l, f)] for f in fams], dim=0)
+    ys = [torch.empty((T, wcat[(l, n)].shape[0]), dtype=torch.bfloat16, device=dev)
+          for (l, n, st, x, y) in wstep.items]
+
+    class _Mm:
+        def run(self):
+            for (l, n, st, x, y), yo in zip(wstep.items, ys):
+                torch.matmul(x, wcat[(l, n)].t(), out=yo)
+    try:
+        t_t, g = time_graph(_Mm(), steps, warmup)
+        del g
+    except Exception as e:          # reference only: never fail the bench on it
+        log(f"hipBLASLt reference skipped: {e}")
+        t_t = float("nan")
+    del dense, bundle, weff, wcat
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"layers": nlayers, "tokens": T,
+            "weightless_ms": t_w * 1e3, "weightless_GBps": wstep.bytes_rd / t_w / 1e9,
+            "weightless_bytes": wstep.bytes_rd,
+            "dense_ms": t_d * 1e3, "dense_GBps": dense_bytes / t_d / 1e9, "dense_bytes": dense_bytes,
+            "hipblaslt_dense_ms": t_t * 1e3, "hipblaslt_dense_GBps": dense_bytes / t_t / 1e9,
+            "weightless_over_dense": t_w / t_d, "weightless_over_hipblaslt_dense": t_w / t_t,
+            "materialize_ms": t_mat * 1e3, "materialize_GBps_written": mat_bytes / t_mat / 1e9}
+
+
 def cpu_baseline(wl, T, budget_s, dev):
     """The fp64 oracle (as it stands) on one layer's four calls of the
     headline workload, repeated until about budget_s of CPU time."""
@@ -365,7 +440,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill"])
+    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill", "dense"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--band-reuse", action="store_true",
                     help="report whether a band-shared W0 re-read by the next layer is served from the 256 MB "
@@ -413,6 +488,11 @@ def main():
     if args.only in ("all", "decode", "decode1"):
         res["decode4_t1"] = decode_section(wl4, 1, args.steps, args.warmup, dev)
         log(f"decode T=1: {res['decode4_t1']['GBps']:.1f} GB/s")
+    if args.only in ("all", "decode", "dense"):
+        res["dense_vs_weightless"] = dense_comparison(wl4, 1, 12, args.steps, args.warmup, dev)
+        log(f"dense comparison: weightless {res['dense_vs_weightless']['weightless_ms']:.3f} ms, dense "
+            f"{res['dense_vs_weightless']['dense_ms']:.3f} ms, hipBLASLt dense "
+            f"{res['dense_vs_weightless']['hipblaslt_dense_ms']:.3f} ms per 12-layer step")
     if args.only in ("all", "decode"):
         res["decode4_t16"] = decode_section(wl4, 16, args.steps, args.warmup, dev)
         log(f"decode T=16: {res['decode4_t16']['GBps']:.1f} GB/s")
