@@ -161,6 +161,24 @@ wl_status weightless_stacked_linear(const wl_bundle *bundle, int32_t layer, int3
                                     const void *d_x, int32_t T, void *d_y,
                                     void *d_ws, size_t ws_bytes, void *stream);
 
+/* Activation of the fused gate|up call (the model's hidden activation). */
+typedef enum {
+  WL_ACT_GELU_TANH = 0, /* 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+  WL_ACT_SILU = 1,      /* x / (1 + exp(-x)) */
+  WL_ACT_GELU_ERF = 2   /* 0.5 x (1 + erf(x / sqrt(2))) */
+} wl_act;
+
+/* The gate|up stack with the MLP activation fused into its epilogue:
+ * h = act(gate) (.) up, bf16 [T, N_gate] at d_h, where gate and up are the
+ * two children of the stacked call, each kept in fp32 until the product is
+ * rounded to bf16 once (so h is not act(bf16(gate)) * bf16(up)).  Requires
+ * N_gate == N_up (else WL_ESHAPE); act outside wl_act gives WL_ERANGE.  The
+ * same launches and workspace as weightless_stacked_linear(WL_STACK_GATE_UP);
+ * d_h must not alias d_x.  It writes half the bytes of the stacked call's
+ * y and saves the separate activation pass over it. */
+wl_status weightless_gate_up_act(const wl_bundle *bundle, int32_t layer, int32_t act, const void *d_x, int32_t T,
+                                 void *d_h, void *d_ws, size_t ws_bytes, void *stream);
+
 /* Workspace bytes weightless_materialize needs for any family of this bundle
  * (the V rows of one family, K x padded rank bf16); 0 on error. */
 size_t weightless_materialize_workspace_bytes(const wl_bundle *bundle);

@@ -22,7 +22,29 @@ per-child results concatenated along N in the order q, k, v / gate, up.  With
 K=V tying on a layer type ("Decompose HF weights: the mixed-attention case"),
 v has no bundle and its output is k's output.
 """
+import math
+
 import numpy as np
+
+# MLP hidden activations by name ("Quality (Gemma 4 31B)" page, "Activation
+# function fix": Gemma 3 and 4 use gelu with the tanh approximation, and a
+# hardcoded silu broke the model; "Add a new model architecture" page, "Route
+# the MLP through config.hidden_activation": the activation is a parameter of
+# the model, never fixed in the layer).  Each is written from its definition.
+ACTIVATIONS = ("gelu_tanh", "silu", "gelu")
+
+
+def activation(name, x):
+    """gelu_tanh: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)));
+    silu: x / (1 + e^-x);  gelu: x Phi(x) = 0.5 x (1 + erf(x / sqrt 2))."""
+    x = np.asarray(x, np.float64)
+    if name == "gelu_tanh":
+        return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+    if name == "silu":
+        return x / (1.0 + np.exp(-x))
+    if name == "gelu":
+        return 0.5 * x * (1.0 + np.vectorize(math.erf, otypes=[np.float64])(x / math.sqrt(2.0)))
+    raise ValueError(f"unknown activation {name!r}")
 
 
 def dense(x, W):
@@ -66,3 +88,9 @@ def stacked(x, children):
         else:
             outs.append(factored(x, *ch))
     return np.concatenate(outs, axis=1)
+
+
+def gate_up_act(x, gate, up, name):
+    """The MLP's gated hidden state h = act(gate x) * (up x), with gate and up
+    each a (W0, s, U, V) bundle evaluated in the factored form."""
+    return activation(name, factored(x, *gate)) * factored(x, *up)

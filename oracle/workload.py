@@ -110,3 +110,8 @@ class OracleWorkload:
         for f in self.families_of(layer, call):
             children.append("dup" if self._tied(layer, f) else self.params(layer, f))
         return forward.stacked(x, children)
+
+    def gate_up_act(self, layer, x, name):
+        """Expected fp64 h = act(gate) * up of one layer's gate|up stack."""
+        return forward.gate_up_act(np.asarray(x, np.float64), self.params(layer, "gate"),
+                                   self.params(layer, "up"), name)

@@ -99,3 +99,35 @@ def test_decompose_mutants_are_caught(monkeypatch, name, attr, mutant):
         except AssertionError:
             caught += 1
     assert caught >= 1, f"{name} passed every decomposition pin"
+
+
+_orig_activation = forward.activation
+
+
+def _tanh_wrong_constant(name, x):
+    x = np.asarray(x, np.float64)
+    if name == "gelu_tanh":
+        return 0.5 * x * (1.0 + np.tanh(np.sqrt(1.0 / np.pi) * (x + 0.044715 * x ** 3)))
+    return _orig_activation(name, x)
+
+
+def _silu_for_everything(name, x):
+    return _orig_activation("silu", x)
+
+
+def _gelu_exact_for_tanh(name, x):
+    return _orig_activation("gelu" if name == "gelu_tanh" else name, x)
+
+
+@pytest.mark.parametrize("mutant", [_tanh_wrong_constant, _silu_for_everything, _gelu_exact_for_tanh])
+def test_activation_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(forward, "activation", mutant)
+    caught = 0
+    for pin, args in [(pins.test_activation_matches_library_routines, ("gelu_tanh",)),
+                      (pins.test_activation_closed_forms, ()),
+                      (pins.test_gate_up_act_brute_force, ())]:
+        try:
+            pin(*args)
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"{mutant.__name__} passed every activation pin"

@@ -382,3 +382,64 @@ def test_compare_accepts_and_rejects():
     nan = y.copy()
     nan[0, 0] = np.nan
     assert not compare.compare(nan, y)["ok"]
+
+
+# ---------------------------------------------------------------------------
+# MLP activation of the fused gate|up epilogue ("Quality (Gemma 4 31B)" page,
+# "Activation function fix"; "Add a new model architecture" page, "Route the
+# MLP through config.hidden_activation")
+# ---------------------------------------------------------------------------
+_ACT_X = np.concatenate([np.linspace(-9.0, 9.0, 1801), np.random.default_rng(7).normal(0, 3, 500)])
+
+
+@pytest.mark.parametrize("name", forward.ACTIVATIONS)
+def test_activation_matches_library_routines(name):
+    """Against independent library routines in fp64: torch's gelu (tanh
+    approximation) and silu, and x * Phi(x) from scipy's normal CDF."""
+    import scipy.stats
+    import torch
+    got = forward.activation(name, _ACT_X)
+    xt = torch.from_numpy(_ACT_X)
+    if name == "gelu_tanh":
+        ref = torch.nn.functional.gelu(xt, approximate="tanh").numpy()
+    elif name == "silu":
+        ref = torch.nn.functional.silu(xt).numpy()
+    else:
+        ref = _ACT_X * scipy.stats.norm.cdf(_ACT_X)
+    assert np.max(np.abs(got - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_activation_closed_forms():
+    """act(0) = 0; act(x) -> x for large x and -> 0 for very negative x;
+    silu(x) = x (1 + tanh(x/2)) / 2; the tanh approximation stays within
+    5e-4 of the exact gelu but is not identical to it."""
+    for name in forward.ACTIVATIONS:
+        assert forward.activation(name, 0.0) == 0.0
+        assert abs(forward.activation(name, 40.0) - 40.0) < 1e-12
+        assert abs(forward.activation(name, -40.0)) < 1e-12
+    x = np.linspace(-8, 8, 3201)
+    assert np.allclose(forward.activation("silu", x), x * (1 + np.tanh(x / 2)) / 2, rtol=0, atol=1e-14)
+    d = np.abs(forward.activation("gelu_tanh", x) - forward.activation("gelu", x))
+    assert 1e-5 < d.max() < 5e-4
+
+
+def test_gate_up_act_brute_force():
+    """h[t][j] = act(g_tj) u_tj with g, u summed by explicit loops and the
+    gelu-tanh written with math.tanh."""
+    rng = np.random.default_rng(11)
+    T, N, K, r = 2, 3, 5, 2
+    gate = (rng.normal(size=(N, K)), rng.normal(1, 0.1, N), rng.normal(size=(N, r)), rng.normal(size=(K, r)))
+    up = (rng.normal(size=(N, K)), rng.normal(1, 0.1, N), rng.normal(size=(N, r)), rng.normal(size=(K, r)))
+    x = rng.normal(size=(T, K))
+    h = forward.gate_up_act(x, gate, up, "gelu_tanh")
+    for t in range(T):
+        for j in range(N):
+            vals = []
+            for W0, s, U, V in (gate, up):
+                acc = s[j] * sum(W0[j, k] * x[t, k] for k in range(K))
+                for q in range(r):
+                    acc += U[j, q] * sum(V[k, q] * x[t, k] for k in range(K))
+                vals.append(acc)
+            g, u = vals
+            gelu = 0.5 * g * (1 + math.tanh(math.sqrt(2 / math.pi) * (g + 0.044715 * g ** 3)))
+            assert abs(h[t, j] - gelu * u) <= 1e-12 * (1 + abs(gelu * u))

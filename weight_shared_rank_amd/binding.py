@@ -17,6 +17,7 @@ LIBPATH = os.path.join(HERE, "libweightless.so")
 FAMILIES = ("q", "k", "v", "o", "gate", "up", "down")
 FAMILY = {f: i for i, f in enumerate(FAMILIES)}
 STACKS = {"qkv": 0, "gate_up": 1}
+ACTS = {"gelu_tanh": 0, "silu": 1, "gelu": 2}
 WL_DTYPE_BF16, WL_DTYPE_F32 = 0, 1
 WL_SRC_W0, WL_SRC_S, WL_SRC_U, WL_SRC_V = 0, 1, 2, 3
 SRC_KIND = {"w0": WL_SRC_W0, "s": WL_SRC_S, "u": WL_SRC_U, "v": WL_SRC_V}
@@ -29,7 +30,7 @@ DECODE_MAX_T = 16
 EXPORTS = ("theta_bundle_arena_bytes", "theta_bundle_load", "theta_bundle_free",
            "weightless_workspace_bytes",
            "weightless_linear", "weightless_stacked_linear", "weightless_out_dim", "wl_last_error",
-           "weightless_materialize_workspace_bytes", "weightless_materialize")
+           "weightless_materialize_workspace_bytes", "weightless_materialize", "weightless_gate_up_act")
 
 
 class WlBundleSpec(ctypes.Structure):
@@ -75,6 +76,7 @@ def lib():
         "wl_last_error": (ctypes.c_char_p, []),
         "weightless_materialize_workspace_bytes": (sz, [vp]),
         "weightless_materialize": (i32, [vp, i32, i32, vp, vp, sz, vp]),
+        "weightless_gate_up_act": (i32, [vp, i32, i32, vp, i32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -222,6 +224,11 @@ class ThetaBundle:
         """The stacked q|k|v or gate|up call over one x."""
         return self._call(lib().weightless_stacked_linear, layer, STACKS[stack], x, y, ws, stream,
                           self.out_dim(layer, stack=stack))
+
+    def gate_up_act(self, layer: int, act: str, x, h=None, ws=None, stream=None):
+        """h = act(gate) * up of one layer's gate|up stack, bf16 [T, N_gate]."""
+        return self._call(lambda hd, l, code, *rest: lib().weightless_gate_up_act(hd, l, ACTS[act], *rest),
+                          layer, 0, x, h, ws, stream, self.out_dim(layer, family="gate"))
 
     def in_dim(self, layer: int, family: str) -> int:
         """K of one family of one layer (from the spec)."""

@@ -28,6 +28,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Activations of the fused gate|up epilogue, fp32 (act codes of the ABI:
+// 0 gelu with the tanh approximation, 1 silu, 2 gelu with erf).
+__device__ __forceinline__ float activation(int act, float x) {
+  if (act == 1) return x / (1.f + __expf(-x));
+  if (act == 2) return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+  const float u = 0.79788456080286536f * (x + 0.044715f * x * x * x);
+  return 0.5f * x * (1.f + tanhf(u));
+}
+
 // D += A * B for a 16x16 output tile over 32 k.  Lane l supplies A row (l & 15)
 // and B column (l & 15), each as 8 bf16 at k-slots 8*(l >> 4) .. +7 (any
 // k-permutation works as long as A and B use the same one); lane l receives

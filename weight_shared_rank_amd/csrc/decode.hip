@@ -241,6 +241,92 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
   }
 }
 
+// Fused gate|up epilogue: h[t][j] = act(gate_j) * up_j with gate_j =
+// s_j p_j + (U_gate z_gate)_j and up_j the same on row N_g + j (children 0 and
+// 1 of the call, N_g rows each).  One workgroup per 16 values of j; its WE
+// waves split the rank steps of both deltas.
+template <int WE>
+__global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const float *p_part,
+                                                               const uint16_t *z_pair, int KS, int act, uint16_t *h,
+                                                               int ldh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int Ng = c.ch[0].N;
+  const int j0 = blockIdx.x * 16;
+  const bool tok_ok = r16 < c.T;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  // wave 0: p partials and s of rows j0 + 4g + i of both halves (rows past
+  // N_g re-read row N_g - 1 of the half and are dropped); summed after the
+  // deltas so all loads are in flight together
+  float part[2][kDecodeMaxSlices][4];
+  float sc[2][4];
+  if (wave == 0 && tok_ok) {
+    const size_t sstride = static_cast<size_t>(c.T) * c.Ntot;
+    const float *pp = p_part + static_cast<size_t>(r16) * c.Ntot;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = c.ch[hf].row_start + min(j0 + 4 * g + i, Ng - 1);
+#pragma unroll
+        for (int s = 0; s < kDecodeMaxSlices; ++s)
+          part[hf][s][i] = pp[static_cast<size_t>(min(s, KS - 1)) * sstride + row];
+        sc[hf][i] = c.s[row];
+      }
+  }
+
+  f32x4 dacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const bool in_rows = j0 + r16 < Ng;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const ChildDesc &ch = c.ch[hf];
+    if (ch.rpad == 0) continue;
+    const uint16_t *urow = ch.U + static_cast<size_t>(in_rows ? j0 + r16 : 0) * ch.rpad + g * 8;
+    const uint16_t *zh = z_pair + static_cast<size_t>(tok_ok ? r16 : 0) * c.Rz + ch.zoff + g * 8;
+    const uint16_t *zl = zh + static_cast<size_t>(c.T) * c.Rz;
+    for (int kk = wave * 32; kk < ch.rpad; kk += 2 * WE * 32) {
+      const int k1 = kk + WE * 32;
+      const bool in1 = k1 < ch.rpad;
+      const int k1c = in1 ? k1 : kk;
+      const u32x4 ua0 = ld16(urow + kk), ua1 = ld16(urow + k1c);
+      const u32x4 h0 = ld16(zh + kk), l0 = ld16(zl + kk), h1 = ld16(zh + k1c), l1 = ld16(zl + k1c);
+      const u32x4 a0 = in_rows ? ua0 : zero4;
+      const u32x4 a1 = (in1 && in_rows) ? ua1 : zero4;
+      dacc[hf] = mfma16x16x32(a0, tok_ok ? h0 : zero4, dacc[hf]);
+      dacc[hf] = mfma16x16x32(a0, tok_ok ? l0 : zero4, dacc[hf]);
+      dacc[hf] = mfma16x16x32(a1, (in1 && tok_ok) ? h1 : zero4, dacc[hf]);
+      dacc[hf] = mfma16x16x32(a1, (in1 && tok_ok) ? l1 : zero4, dacc[hf]);
+    }
+  }
+  __shared__ f32x4 red[WE][2][64];
+  red[wave][0][lane] = dacc[0];
+  red[wave][1][lane] = dacc[1];
+  __syncthreads();
+  if (wave != 0 || !tok_ok) return;
+  float y[2][4];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x4 d = red[0][hf][lane];
+#pragma unroll
+    for (int w = 1; w < WE; ++w) d += red[w][hf][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p = part[hf][0][i];
+#pragma unroll
+      for (int s = 1; s < kDecodeMaxSlices; ++s)
+        if (s < KS) p += part[hf][s][i];
+      y[hf][i] = sc[hf][i] * p + d[i];
+    }
+  }
+  uint16_t *hrow = h + static_cast<size_t>(r16) * ldh;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = j0 + 4 * g + i;
+    if (j < Ng) hrow[j] = f32_to_bf16(activation(act, y[0][i]) * y[1][i]);
+  }
+}
+
 }  // namespace
 
 int decode_k_slices(int Ntot, int Rz, int K) {
@@ -253,15 +339,22 @@ int decode_k_slices(int Ntot, int Rz, int K) {
   return max(1, min(ks, kDecodeMaxSlices));
 }
 
-hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream) {
+hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream, int act,
+                         uint16_t *h, int ldh) {
   const int KS = decode_k_slices(c.Ntot, c.Rz, c.K);
   const int nt_w0 = (c.Ntot + 15) / 16, nt_vt = (c.Rz + 15) / 16;
   hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nt_vt + nt_w0 * KS), dim3(kStreamWaves * 64),
                      0, stream, c, p_part, z_pair, nt_vt, KS);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((epilogue_kernel<kEpiWaves>), dim3(nt_w0), dim3(kEpiWaves * 64), 0, stream, c,
-                     static_cast<const float *>(p_part), static_cast<const uint16_t *>(z_pair), KS);
+  if (act < 0) {
+    hipLaunchKernelGGL((epilogue_kernel<kEpiWaves>), dim3(nt_w0), dim3(kEpiWaves * 64), 0, stream, c,
+                       static_cast<const float *>(p_part), static_cast<const uint16_t *>(z_pair), KS);
+  } else {
+    const int nt = (c.ch[0].N + 15) / 16;
+    hipLaunchKernelGGL((act_epilogue_kernel<kEpiWaves>), dim3(nt), dim3(kEpiWaves * 64), 0, stream, c,
+                       static_cast<const float *>(p_part), static_cast<const uint16_t *>(z_pair), KS, act, h, ldh);
+  }
   return hipGetLastError();
 }
 

@@ -45,8 +45,11 @@ struct CallDesc {
 // partials p_part [KS][T][Ntot] (fp32) and z = V^T x (V^T rows are not
 // split) as a bf16 hi/lo pair z_pair [2][T][Rz]; launch 2 sums the partials
 // and applies the scale and the U z epilogue.
+// act >= 0: the call is gate|up (children 0 and 1 with equal N) and the
+// epilogue writes h [T][ldh] = act(gate) * up instead of y.
 int decode_k_slices(int Ntot, int Rz, int K);
-hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream);
+hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream, int act = -1,
+                         uint16_t *h = nullptr, int ldh = 0);
 
 // Prefill path (T > 16): Z = X V into zbuf [T][Rz] (bf16), then the main
 // GEMM with the scale and rank-r epilogue.  GEMMs with few rows split K and
@@ -55,8 +58,10 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hip
 // zero_row points at >= 16 zero bytes (used to mask rows and k columns
 // outside an operand).
 size_t prefill_partial_bytes(int Ntot, int Rz, int rmax, int K, int T);
+// act >= 0: gate|up call (children 0 and 1 with equal N) writing
+// h [T][ldh] = act(gate) * up instead of y.
 hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const uint16_t *zero_row,
-                          hipStream_t stream);
+                          hipStream_t stream, int act = -1, uint16_t *h = nullptr, int ldh = 0);
 
 // Effective weight: out[N][K] (bf16) = s (.) W0 + U V^T, with V given as
 // rows [K][rpad] (ranks contiguous) and U as [N][rpad]; rpad may be 0.

@@ -74,6 +74,7 @@ enum Mode : int32_t {
   kFused = 1,      // Y = child map of bf16(s (.) acc + Z U^T)
   kPartial = 2,    // P[slice][T][M] = acc (fp32); slice ksplit (if nchild) = Z U^T
   kAddScaled = 3,  // Y = bf16(acc + s[t] * W[t][m]), [T][ldy] (effective-weight materialization)
+  kFusedAct = 4,   // paired gate|up rows: H = bf16(act(s (.) gate + dg) * (s (.) up + du)), [T][ldh]
 };
 
 struct GemmArgs {
@@ -98,6 +99,10 @@ struct GemmArgs {
   float *P;           // partials [ksplit (+1 for the delta)][T][M]
   const uint16_t *W;  // kAddScaled: [T][ldw] bf16, scaled by s[t] and added
   int64_t ldw;
+  int32_t pair;       // > 0: rows are paired gate|up with this many gate rows
+  int32_t act;        // kFusedAct: activation code
+  uint16_t *H;        // kFusedAct: [T][ldh] bf16
+  int32_t ldh;
   int32_t nchild;
   ChildDesc ch[kMaxChildren];
 };
@@ -214,7 +219,20 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
     t = u % a.nT;
     sl = a.ksplit;
   }
-  const int m0 = f * BM, n0 = t * BN;
+  const int n0 = t * BN;
+  // Tile rows.  Plain: rows f*BM + v.  Paired (gate|up with the activation
+  // fused): v < BM/2 is gate row f*BM/2 + v and v >= BM/2 is up row
+  // pair + f*BM/2 + v - BM/2, so gate and up of one output column meet in
+  // one tile.  valid() counts rows of the operand; 4-row groups never
+  // straddle the two halves.
+  constexpr int HB = BM / 2;
+  auto actual = [&](int v) -> int {
+    return a.pair ? (v >= HB ? a.pair : 0) + f * HB + (v & (HB - 1)) : f * BM + v;
+  };
+  auto nvalid = [&](int v, int n) -> int {  // how many of rows v..v+n-1 exist
+    const int lim = a.pair ? a.pair - (f * HB + (v & (HB - 1))) : a.M - (f * BM + v);
+    return max(0, min(n, lim));
+  };
 
   f32x4 acc[TL::FM][TL::FN];
 #pragma unroll
@@ -230,8 +248,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
     for (int q = 0; q < TL::LPW; ++q) {
       const int gq = wave * TL::LPW + q;
       if (gq < TL::GA) {
-        const int row = m0 + gq * 8 + lrow;
-        rp[q] = row < a.M ? a.A + row * a.lda + lchunk * 8 : nullptr;
+        const int v = gq * 8 + lrow;
+        rp[q] = nvalid(v, 1) ? a.A + actual(v) * a.lda + lchunk * 8 : nullptr;
       } else {
         const int row = n0 + (gq - TL::GA) * 8 + lrow;
         rp[q] = row < a.T ? a.B + row * a.ldb + lchunk * 8 : nullptr;
@@ -242,31 +260,35 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
     segment<BM, BN, WM, WN, NST>(acc, rp, a.K, sb, se, a.zero_row, lds);
   }
 
-  if (a.mode == kFused) {
-    // scale by s (rows outside [0, M) are never stored)
+  const bool fused = a.mode == kFused || a.mode == kFusedAct;
+  if (fused) {
+    // scale by s (rows outside the operand are never stored)
 #pragma unroll
     for (int i = 0; i < TL::FM; ++i) {
-      const int row = m0 + wm * TL::TM + i * 16 + g * 4;
+      const int v = wm * TL::TM + i * 16 + g * 4;
+      const int nv = nvalid(v, 4), row = actual(v);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float sc = row + e < a.M ? a.s[row + e] : 0.f;
+        const float sc = e < nv ? a.s[row + e] : 0.f;
 #pragma unroll
         for (int j = 0; j < TL::FN; ++j) acc[i][j][e] *= sc;
       }
     }
   }
-  if (a.mode == kFused || delta_slice) {
+  if (fused || delta_slice) {
     // delta = Z U^T for every child with rows in this tile
     for (int ci = 0; ci < a.nchild; ++ci) {
       const ChildDesc &ch = a.ch[ci];
-      if (ch.rpad == 0 || m0 >= ch.row_start + ch.N || m0 + BM <= ch.row_start) continue;
+      if (ch.rpad == 0) continue;
+      if (!a.pair && (f * BM >= ch.row_start + ch.N || f * BM + BM <= ch.row_start)) continue;
       const uint16_t *rp[TL::LPW];
 #pragma unroll
       for (int q = 0; q < TL::LPW; ++q) {
         const int gq = wave * TL::LPW + q;
         if (gq < TL::GA) {
-          const int row = m0 + gq * 8 + lrow;
-          const bool in = row >= ch.row_start && row < ch.row_start + ch.N;
+          const int v = gq * 8 + lrow;
+          const int row = actual(v);
+          const bool in = nvalid(v, 1) && row >= ch.row_start && row < ch.row_start + ch.N;
           rp[q] = in ? ch.U + static_cast<int64_t>(row - ch.row_start) * ch.rpad + lchunk * 8 : nullptr;
         } else {
           const int row = n0 + (gq - TL::GA) * 8 + lrow;
@@ -277,7 +299,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
     }
   }
 
-  // lane holds rows m0 + wm*TM + 16i + 4g + e, token n0 + wn*TN + 16j + r16
+  // lane holds tile rows v = wm*TM + 16i + 4g + e, token n0 + wn*TN + 16j + r16
   if (a.mode == kPartial) {
     float *P = a.P + static_cast<size_t>(sl) * a.T * a.M;
 #pragma unroll
@@ -287,19 +309,57 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
       float *prow = P + static_cast<size_t>(tok) * a.M;
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i) {
-        const int row = m0 + wm * TL::TM + i * 16 + g * 4;
-        if (row + 3 < a.M && (a.M & 3) == 0) {
+        const int v = wm * TL::TM + i * 16 + g * 4;
+        const int nv = nvalid(v, 4), row = actual(v);
+        if (nv == 4 && ((a.M | row) & 3) == 0) {
           *reinterpret_cast<f32x4 *>(prow + row) = acc[i][j];
         } else {
-          for (int e = 0; e < 4; ++e)
-            if (row + e < a.M) prow[row + e] = acc[i][j][e];
+          for (int e = 0; e < nv; ++e) prow[row + e] = acc[i][j][e];
         }
       }
     }
     return;
   }
 
-  // store: lane holds rows m0 + wm*TM + 16i + 4g + e, token n0 + wn*TN + 16j + r16
+  if (a.mode == kFusedAct) {
+    // the up half's waves hand their values to the gate half's waves (same
+    // lane, same i and j) through LDS, which the K loop no longer uses
+    f32x4 *xch = reinterpret_cast<f32x4 *>(lds);
+    const bool up_half = wm >= WM / 2;
+    const int pw = (wm % (WM / 2)) * WN + wn;
+    if (up_half) {
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) xch[((pw * TL::FM + i) * TL::FN + j) * 64 + lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (up_half) return;
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) {
+      const int tok = n0 + wn * TL::TN + j * 16 + r16;
+      if (tok >= a.T) continue;
+      uint16_t *hrow = a.H + static_cast<int64_t>(tok) * a.ldh;
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i) {
+        const int v = wm * TL::TM + i * 16 + g * 4;  // < BM/2: a gate row
+        const int nv = nvalid(v, 4), jj = actual(v);
+        const f32x4 u = xch[((pw * TL::FM + i) * TL::FN + j) * 64 + lane];
+        uint16_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(activation(a.act, acc[i][j][e]) * u[e]);
+        if (nv == 4 && ((a.ldh | jj) & 3) == 0) {
+          *reinterpret_cast<uint2 *>(hrow + jj) =
+              make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+        } else {
+          for (int e = 0; e < nv; ++e) hrow[jj + e] = o[e];
+        }
+      }
+    }
+    return;
+  }
+
+  // store: y through the child map (fused), or plain rows
 #pragma unroll
   for (int j = 0; j < TL::FN; ++j) {
     const int tok = n0 + wn * TL::TN + j * 16 + r16;
@@ -307,8 +367,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
     uint16_t *yrow = a.Y + static_cast<int64_t>(tok) * a.ldy;
 #pragma unroll
     for (int i = 0; i < TL::FM; ++i) {
-      const int row = m0 + wm * TL::TM + i * 16 + g * 4;
-      if (row >= a.M) continue;
+      const int v = wm * TL::TM + i * 16 + g * 4;
+      const int nv = nvalid(v, 4), row = actual(v);
+      if (nv == 0) continue;
       uint16_t o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(acc[i][j][e]);
@@ -319,20 +380,18 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
         const uint16_t *wrow = a.W + static_cast<int64_t>(tok) * a.ldw;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (row + e < a.M) o[e] = f32_to_bf16(acc[i][j][e] + sc * bf16_to_f32(wrow[row + e]));
+          if (e < nv) o[e] = f32_to_bf16(acc[i][j][e] + sc * bf16_to_f32(wrow[row + e]));
       }
       if (a.mode == kStoreBf16 || a.mode == kAddScaled) {
-        if (row + 3 < a.M && ((a.ldy | row) & 3) == 0) {
+        if (nv == 4 && ((a.ldy | row) & 3) == 0) {
           *reinterpret_cast<uint2 *>(yrow + row) =
               make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
         } else {
-          for (int e = 0; e < 4; ++e)
-            if (row + e < a.M) yrow[row + e] = o[e];
+          for (int e = 0; e < nv; ++e) yrow[row + e] = o[e];
         }
       } else {
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < nv; ++e) {
           const int r = row + e;
-          if (r >= a.M) break;
           int ci = 0;
           while (ci + 1 < a.nchild && r >= a.ch[ci + 1].row_start) ++ci;
           const ChildDesc &ch = a.ch[ci];
@@ -367,7 +426,29 @@ struct FinishArgs {
   int32_t ldy;
   int32_t nchild;
   ChildDesc ch[kMaxChildren];
+  int32_t act, pair;  // act >= 0: h = act(gate) * up into H, pair = gate rows
+  uint16_t *H;
+  int32_t ldh;
 };
+
+// One output value of the split path at row r, token tok:
+// s_r sum_{slice < ksplit} P[slice][tok][r] + P[ksplit][tok][r] (the delta).
+__device__ __forceinline__ float finished(const FinishArgs &a, int tok, int r) {
+  const size_t plane = static_cast<size_t>(a.T) * a.M;
+  const float *p = a.P + static_cast<size_t>(tok) * a.M + r;
+  float acc = 0.f;
+  for (int s = 0; s < a.ksplit; ++s) acc += p[s * plane];
+  return a.s[r] * acc + (a.has_delta ? p[a.ksplit * plane] : 0.f);
+}
+
+// h[tok][j] = act(gate_j) * up_j for the paired gate|up call on the split path.
+__global__ void finish_act_kernel(FinishArgs a) {
+  const long id = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (id >= static_cast<long>(a.pair) * a.T) return;
+  const int tok = static_cast<int>(id / a.pair), j = static_cast<int>(id % a.pair);
+  const float gv = finished(a, tok, j), uv = finished(a, tok, a.pair + j);
+  a.H[static_cast<size_t>(tok) * a.ldh + j] = f32_to_bf16(activation(a.act, gv) * uv);
+}
 
 __global__ void finish_kernel(FinishArgs a) {
   const int groups = (a.M + 3) / 4;
@@ -502,7 +583,7 @@ size_t prefill_partial_bytes(int Ntot, int Rz, int rmax, int K, int T) {
 }
 
 hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const uint16_t *zero_row,
-                          hipStream_t stream) {
+                          hipStream_t stream, int act, uint16_t *h, int ldh) {
   hipError_t e;
   if (c.Rz > 0) {
     GemmArgs a{};
@@ -547,9 +628,18 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const 
   a.P = pbuf;
   a.nchild = c.nchild;
   for (int i = 0; i < c.nchild; ++i) a.ch[i] = c.ch[i];
-  const Plan p = plan_gemm(c.Ntot, c.K, c.T, delta_steps(c));
+  Plan p = plan_gemm(c.Ntot, c.K, c.T, delta_steps(c));
+  if (act >= 0) {
+    // gate|up with the activation fused: tiles hold BM/2 gate rows and the
+    // matching BM/2 up rows
+    a.pair = c.ch[0].N;
+    a.act = act;
+    a.H = h;
+    a.ldh = ldh;
+    p.nM = (a.pair + kTiles[p.tile].BM / 2 - 1) / (kTiles[p.tile].BM / 2);
+  }
   if (p.ksplit == 1) {
-    a.mode = kFused;
+    a.mode = act >= 0 ? kFusedAct : kFused;
     return launch_planned(a, p, stream);
   }
   // K slices plus (if any child has a rank) one delta slice per tile
@@ -569,6 +659,16 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const 
   fa.ldy = c.ldy;
   fa.nchild = c.nchild;
   for (int i = 0; i < c.nchild; ++i) fa.ch[i] = c.ch[i];
+  if (act >= 0) {
+    fa.act = act;
+    fa.pair = c.ch[0].N;
+    fa.H = h;
+    fa.ldh = ldh;
+    const long threads = static_cast<long>(fa.pair) * c.T;
+    hipLaunchKernelGGL(finish_act_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream,
+                       fa);
+    return hipGetLastError();
+  }
   const long threads = static_cast<long>((c.Ntot + 3) / 4) * c.T;
   hipLaunchKernelGGL(finish_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream, fa);
   return hipGetLastError();

@@ -344,11 +344,18 @@ wl_status resolve(const wl_bundle *h, int32_t layer, int32_t family, int32_t sta
   return WL_OK;
 }
 
+// act >= 0: the gate|up stack with the activation fused; d_y then receives
+// h = act(gate) * up, [T, N_gate].
 wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t stack, const void *d_x,
-                   int32_t T, void *d_y, void *d_ws, size_t ws_bytes, void *stream) {
+                   int32_t T, void *d_y, void *d_ws, size_t ws_bytes, void *stream, int32_t act = -1) {
   Resolved rv;
   wl_status st = resolve(h, layer, family, stack, rv);
   if (st != WL_OK) return st;
+  if (act >= 0) {
+    if (rv.c.nchild != 2 || rv.c.ch[0].N != rv.c.ch[1].N)
+      return fail(WL_ESHAPE, "gate and up of layer %d must have equal out_dim", layer);
+    rv.out_dim = rv.c.ch[0].N;
+  }
   if (T < 0) return fail(WL_EINVAL, "T = %d is negative", T);
   if (T > kMaxDim) return fail(WL_ESHAPE, "T = %d too large", T);
   if (T == 0) return WL_OK;
@@ -369,8 +376,10 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *ws = static_cast<uint8_t *>(d_ws);
   hipError_t e;
+  uint16_t *hout = act >= 0 ? static_cast<uint16_t *>(d_y) : nullptr;
   if (T <= wl::kDecodeMaxT)
-    e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), reinterpret_cast<uint16_t *>(ws + ws_p_part_bytes(h->lo, T)), s);
+    e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), reinterpret_cast<uint16_t *>(ws + ws_p_part_bytes(h->lo, T)),
+                          s, act, hout, rv.out_dim);
   else {
     // internal guard: this call's split partials fit the region sized for
     // the largest call shape of the bundle
@@ -380,7 +389,8 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
       return fail(WL_ENOSPACE, "internal: prefill partials of this call exceed the planned workspace");
     e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws),
                            reinterpret_cast<float *>(ws + ws_prefill_z_bytes(h->lo, T)),
-                           reinterpret_cast<const uint16_t *>(h->arena + h->lo.zero_off), s);
+                           reinterpret_cast<const uint16_t *>(h->arena + h->lo.zero_off), s, act, hout,
+                           rv.out_dim);
   }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return WL_OK;
@@ -547,6 +557,12 @@ wl_status weightless_stacked_linear(const wl_bundle *bundle, int32_t layer, int3
                                     void *d_y, void *d_ws, size_t ws_bytes, void *stream) {
   if (stack < 0) return fail(WL_ERANGE, "stack %d out of range", stack);
   return run_call(bundle, layer, -1, stack, d_x, T, d_y, d_ws, ws_bytes, stream);
+}
+
+wl_status weightless_gate_up_act(const wl_bundle *bundle, int32_t layer, int32_t act, const void *d_x, int32_t T,
+                                 void *d_h, void *d_ws, size_t ws_bytes, void *stream) {
+  if (act < WL_ACT_GELU_TANH || act > WL_ACT_GELU_ERF) return fail(WL_ERANGE, "activation %d out of range", act);
+  return run_call(bundle, layer, -1, WL_STACK_GATE_UP, d_x, T, d_h, d_ws, ws_bytes, stream, act);
 }
 
 size_t weightless_materialize_workspace_bytes(const wl_bundle *bundle) {
