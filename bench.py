@@ -307,6 +307,42 @@ def dense_comparison(wl, T, nlayers, steps, warmup, dev):
             "materialize_ms": t_mat * 1e3, "materialize_GBps_written": mat_bytes / t_mat / 1e9}
 
 
+def gate_up_act_section(wl, T, steps, warmup, dev, act="gelu_tanh"):
+    """The gate|up stack of every layer with the MLP activation fused
+    (weightless_gate_up_act, h [T, N]) against the stacked call (y [T, 2N])
+    followed by the activation and product in torch: graph-replayed, per
+    call."""
+    import torch
+    import torch.nn.functional as F
+    import synth.device as sdev
+    bundle = sdev.load(wl, dev)
+    n = wl.shape(0, "gate")[0]
+    xs = [wl.x(l, "gate_up", T, dev) for l in range(wl.num_layers)]
+    ys = [torch.empty((T, 2 * n), dtype=torch.bfloat16, device=dev) for _ in xs]
+    hs = [torch.empty((T, n), dtype=torch.bfloat16, device=dev) for _ in xs]
+    ws = bundle.workspace(T)
+
+    class _Fused:
+        def run(self):
+            for l, (x, h) in enumerate(zip(xs, hs)):
+                bundle.gate_up_act(l, act, x, h=h, ws=ws)
+
+    class _Unfused:
+        def run(self):
+            for l, (x, y, h) in enumerate(zip(xs, ys, hs)):
+                bundle.stacked(l, "gate_up", x, y=y, ws=ws)
+                torch.mul(F.gelu(y[:, :n], approximate="tanh"), y[:, n:], out=h)
+    t_f, g = time_graph(_Fused(), steps, warmup)
+    del g
+    t_u, g = time_graph(_Unfused(), steps, warmup)
+    del g, bundle
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    L = wl.num_layers
+    return {"tokens": T, "layers": L, "fused_us_per_call": t_f / L * 1e6, "unfused_us_per_call": t_u / L * 1e6,
+            "speedup": t_u / t_f, "h_bytes_written_per_call": 2 * T * n, "y_bytes_written_per_call": 4 * T * n}
+
+
 def cpu_baseline(wl, T, budget_s, dev):
     """The fp64 oracle (as it stands) on one layer's four calls of the
     headline workload, repeated until about budget_s of CPU time."""
@@ -440,7 +476,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill", "dense"])
+    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill", "dense", "act"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--band-reuse", action="store_true",
                     help="report whether a band-shared W0 re-read by the next layer is served from the 256 MB "
@@ -493,6 +529,10 @@ def main():
         log(f"dense comparison: weightless {res['dense_vs_weightless']['weightless_ms']:.3f} ms, dense "
             f"{res['dense_vs_weightless']['dense_ms']:.3f} ms, hipBLASLt dense "
             f"{res['dense_vs_weightless']['hipblaslt_dense_ms']:.3f} ms per 12-layer step")
+    if args.only in ("all", "decode", "act"):
+        res["gate_up_act_decode"] = gate_up_act_section(wl4, 1, args.steps, args.warmup, dev)
+        log(f"gate|up act, decode T=1: fused {res['gate_up_act_decode']['fused_us_per_call']:.1f} us, unfused "
+            f"{res['gate_up_act_decode']['unfused_us_per_call']:.1f} us per call")
     if args.only in ("all", "decode"):
         res["decode4_t16"] = decode_section(wl4, 16, args.steps, args.warmup, dev)
         log(f"decode T=16: {res['decode4_t16']['GBps']:.1f} GB/s")
@@ -502,6 +542,9 @@ def main():
     if args.only in ("all", "prefill"):
         res["prefill5"] = prefill_section(synth.workload(5), 512, CALLS, max(2, args.steps // 4), 2, dev)
         log(f"prefill w5: {res['prefill5']['TFLOPs']:.1f} TFLOP/s")
+        res["gate_up_act_prefill"] = gate_up_act_section(synth.workload(5), 512, max(2, args.steps // 4), 2, dev)
+        log(f"gate|up act, prefill T=512: fused {res['gate_up_act_prefill']['fused_us_per_call']:.1f} us, unfused "
+            f"{res['gate_up_act_prefill']['unfused_us_per_call']:.1f} us per call")
         singles = tuple((f, (f,)) for f in synth.FAMILIES)
         res["prefill3"] = prefill_section(synth.workload(3), 2048, singles, args.steps, args.warmup, dev)
         log(f"prefill w3: {res['prefill3']['TFLOPs']:.1f} TFLOP/s")
