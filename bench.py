@@ -38,9 +38,10 @@ def log(msg):
     sys.stderr.flush()
 
 
-def call_bytes(wl, layer, fams, T):
+def call_bytes(wl, layer, fams, T, w0_format="bf16"):
     """Algorithmic bytes a call must read: 2NK (W0) + 4N (s) + 2Nr (U) +
-    2Kr (V^T) per child, plus 2TK (x) once; and the bytes it writes (2TN)."""
+    2Kr (V^T) per child, plus 2TK (x) once; and the bytes it writes (2TN).
+    An FP8 W0 is NK bytes of codes plus 4N of row scales."""
     lt = wl.layer_types[layer]
     rd = 0
     wr = 0
@@ -51,7 +52,8 @@ def call_bytes(wl, layer, fams, T):
             wr += 2 * T * N
             continue
         r = wl.clamped_rank(lt, f)
-        rd += 2 * N * K + 4 * N + 2 * N * r + 2 * K * r
+        w0 = N * K + 4 * N if w0_format == "fp8" else 2 * N * K
+        rd += w0 + 4 * N + 2 * N * r + 2 * K * r
         wr += 2 * T * N
     return rd + 2 * T * K, wr
 
@@ -72,7 +74,7 @@ class Step:
     """Every call of every layer (or of the given layers), with preallocated
     inputs and outputs."""
 
-    def __init__(self, wl, bundle, T, calls, dev, layers=None):
+    def __init__(self, wl, bundle, T, calls, dev, layers=None, w0_format="bf16"):
         import torch
         self.items = []
         self.bytes_rd = 0
@@ -87,7 +89,7 @@ class Step:
                 stacked = len(fams) > 1
                 width = bundle.out_dim(layer, stack=name) if stacked else bundle.out_dim(layer, family=name)
                 y = torch.empty((T, width), dtype=torch.bfloat16, device=dev)
-                rd, wr = call_bytes(wl, layer, fams_here, T)
+                rd, wr = call_bytes(wl, layer, fams_here, T, w0_format)
                 fl = call_flops(wl, layer, fams_here, T)
                 self.items.append((layer, name, stacked, x, y))
                 self.bytes_rd += rd
@@ -182,13 +184,13 @@ def traffic_from_profile(key, sha):
     return rec.get("hbm_bytes_per_call")
 
 
-def decode_section(wl, T, steps, warmup, dev, reps=3):
+def decode_section(wl, T, steps, warmup, dev, reps=3, w0_format="bf16"):
     import synth.device as sdev
     import torch
-    log(f"load {wl.name}")
-    bundle = sdev.load(wl, dev)
+    log(f"load {wl.name} ({w0_format} W0)")
+    bundle = sdev.load(wl, dev, w0_format=w0_format)
     torch.cuda.synchronize()
-    step = Step(wl, bundle, T, CALLS, dev)
+    step = Step(wl, bundle, T, CALLS, dev, w0_format=w0_format)
     t_step, g = time_graph(step, steps, warmup)
     durs = time_launches(step, reps)
     launches = sum(pc["calls"] for pc in step.per_call.values())
@@ -476,7 +478,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill", "dense", "act"])
+    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill", "dense", "act", "fp8"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--band-reuse", action="store_true",
                     help="report whether a band-shared W0 re-read by the next layer is served from the 256 MB "
@@ -524,6 +526,10 @@ def main():
     if args.only in ("all", "decode", "decode1"):
         res["decode4_t1"] = decode_section(wl4, 1, args.steps, args.warmup, dev)
         log(f"decode T=1: {res['decode4_t1']['GBps']:.1f} GB/s")
+    if args.only in ("all", "decode", "fp8"):
+        res["decode4_fp8_t1"] = decode_section(wl4, 1, args.steps, args.warmup, dev, w0_format="fp8")
+        log(f"decode T=1, FP8 W0: {res['decode4_fp8_t1']['GBps']:.1f} GB/s, "
+            f"{res['decode4_fp8_t1']['step_s'] * 1e3:.3f} ms per step")
     if args.only in ("all", "decode", "dense"):
         res["dense_vs_weightless"] = dense_comparison(wl4, 1, 12, args.steps, args.warmup, dev)
         log(f"dense comparison: weightless {res['dense_vs_weightless']['weightless_ms']:.3f} ms, dense "

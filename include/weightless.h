@@ -79,7 +79,16 @@ typedef enum { WL_SRC_W0 = 0, WL_SRC_S = 1, WL_SRC_U = 2, WL_SRC_V = 3 } wl_src_
  *  W0 grouping: attention families (q, k, v, o) have one W0 per
  *    (band, layer type, family); MLP families (gate, up, down) one W0 per
  *    (band, family) shared by both layer types, so their out/in dims must agree
- *    across types.  W0 exists only for (band, type) pairs that hold a layer. */
+ *    across types.  W0 exists only for (band, type) pairs that hold a layer.
+ *  w0_format: WL_W0_BF16 (0; a zero-initialized spec) stores W0 as given;
+ *    WL_W0_FP8 stores each W0 row as OCP E4M3 codes with one power-of-two
+ *    scale q = 2^e per row (e the smallest integer with max|w| <= 448 * 2^e;
+ *    code = E4M3(w / q), round to nearest even), coded by theta_bundle_load
+ *    from bf16 device sources.  The bundle then stands for W0 = E4M3(code) * q
+ *    (the quantized-shared-block variant, "Quality (Gemma 4 31B)" page,
+ *    "Verdict"): decode reads one byte per W0 element; prefill and
+ *    weightless_materialize expand the call's rows to bf16 in the workspace. */
+typedef enum { WL_W0_BF16 = 0, WL_W0_FP8 = 1 } wl_w0_format;
 typedef struct {
   int32_t num_layers;
   int32_t num_bands;
@@ -89,10 +98,12 @@ typedef struct {
   int32_t in_dim[WL_MAX_LAYER_TYPES][WL_NUM_FAMILIES];
   int32_t rank[WL_MAX_LAYER_TYPES][WL_NUM_FAMILIES];
   uint32_t k_eq_v_type_mask;
+  int32_t w0_format;
 } wl_bundle_spec;
 
 /* One source tensor handed to theta_bundle_load.
  *  kind W0: index = band, layer_type = type (0 for MLP families), bf16 [N, K]
+ *           (on the device for WL_W0_FP8 bundles)
  *  kind S:  index = layer, float32 [N]
  *  kind U:  index = layer, bf16 [N, r]
  *  kind V:  index = layer, bf16 [K, r]   (V, not V^T: y = U (V^T x))

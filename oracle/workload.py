@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from . import forward
+from . import forward, quant
 from .decompose import band_members, decompose_band
 
 _CALLS = {"qkv": ("q", "k", "v"), "o": ("o",), "gate_up": ("gate", "up"), "down": ("down",)}
@@ -24,19 +24,26 @@ def to64(t):
 
 
 class OracleWorkload:
-    def __init__(self, wl, device="cpu", cache_w0=4):
+    def __init__(self, wl, device="cpu", cache_w0=4, w0_format="bf16"):
+        """w0_format "fp8": the bundle stands for W0 coded per row in E4M3
+        with a power-of-two scale (oracle.quant); every W0 the oracle uses is
+        that dequantized block."""
         self.wl = wl
         self.device = device
         self._dec = {}
         self._w0 = {}
         self._cache_w0 = cache_w0
+        self.w0_format = w0_format
 
     def w0(self, band, ltype, fam):
         key = (band, ltype if fam in ("q", "k", "v", "o") else 0, fam)
         if key not in self._w0:
             if len(self._w0) >= self._cache_w0:
                 self._w0.pop(next(iter(self._w0)))
-            self._w0[key] = to64(self.wl.w0(band, ltype, fam, self.device))
+            w = to64(self.wl.w0(band, ltype, fam, self.device))
+            if self.w0_format == "fp8":
+                w = quant.dequantize(*quant.quantize_rows(w))
+            self._w0[key] = w
         return self._w0[key]
 
     def prefetch_decompositions(self, keys, workers=8):

@@ -11,10 +11,10 @@ from typing import Callable, Optional
 from weight_shared_rank_amd import binding
 
 
-def spec_of(wl) -> binding.WlBundleSpec:
+def spec_of(wl, w0_format="bf16") -> binding.WlBundleSpec:
     ranks = {key: min(wl.rank, *wl.dims[key]) for key in wl.dims}
     return binding.make_spec(wl.num_layers, wl.num_bands, dict(wl.dims), ranks,
-                             list(wl.layer_types), wl.k_eq_v_types)
+                             list(wl.layer_types), wl.k_eq_v_types, w0_format=w0_format)
 
 
 def sources_of(wl, device="cuda", tensors: Optional[Callable] = None, layers=None):
@@ -51,5 +51,6 @@ def sources_of(wl, device="cuda", tensors: Optional[Callable] = None, layers=Non
     return srcs
 
 
-def load(wl, device="cuda", tensors=None, stream=None) -> binding.ThetaBundle:
-    return binding.ThetaBundle(spec_of(wl), sources_of(wl, device, tensors), device=device, stream=stream)
+def load(wl, device="cuda", tensors=None, stream=None, w0_format="bf16") -> binding.ThetaBundle:
+    return binding.ThetaBundle(spec_of(wl, w0_format), sources_of(wl, device, tensors), device=device,
+                               stream=stream)

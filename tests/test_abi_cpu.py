@@ -195,3 +195,29 @@ def test_empty_bundle_and_null_handles(L):
     assert L.weightless_out_dim(None, 0, 0, -1) == 0
     assert L.weightless_materialize_workspace_bytes(None) == 0
     assert L.weightless_materialize(None, 0, 0, FAKE_ARENA, FAKE_ARENA, 1 << 20, None) == -1
+
+
+def test_fp8_spec_and_sources(L):
+    """w0_format: unknown values are rejected; an FP8 bundle is smaller (one
+    byte per W0 element, rows padded to 16 bytes, one fp32 scale per row) and
+    takes W0 only from device memory (checked before any HIP call)."""
+    import synth
+    import synth.device as sdev
+    wl = synth.workload(1)
+    sp = sdev.spec_of(wl)
+    sp8 = sdev.spec_of(wl, "fp8")
+    n16, n8 = L.theta_bundle_arena_bytes(ctypes.byref(sp)), L.theta_bundle_arena_bytes(ctypes.byref(sp8))
+    w0 = 4096 * 1152
+    assert n16 - n8 == w0 - 4096 * 4
+    sp8.w0_format = 2
+    assert L.theta_bundle_arena_bytes(ctypes.byref(sp8)) == 0
+    assert "w0_format" in binding.last_error()
+    sp8.w0_format = 1
+    import numpy as np
+    host = np.zeros((4096, 1152), np.uint16)
+    srcs = (binding.WlSrc * 1)()
+    srcs[0].kind, srcs[0].index, srcs[0].layer_type, srcs[0].family = 0, 0, 0, binding.FAMILY["up"]
+    srcs[0].dtype, srcs[0].on_device, srcs[0].ptr = 0, 0, host.ctypes.data
+    h = ctypes.c_void_p()
+    assert L.theta_bundle_load(ctypes.byref(sp8), srcs, 1, FAKE_ARENA, n8, None, ctypes.byref(h)) == -1
+    assert "device" in binding.last_error()

@@ -443,3 +443,63 @@ def test_gate_up_act_brute_force():
             g, u = vals
             gelu = 0.5 * g * (1 + math.tanh(math.sqrt(2 / math.pi) * (g + 0.044715 * g ** 3)))
             assert abs(h[t, j] - gelu * u) <= 1e-12 * (1 + abs(gelu * u))
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) shared block with per-row power-of-two scales (oracle.quant)
+# ---------------------------------------------------------------------------
+def test_e4m3_table_matches_torch():
+    """Every code's value against torch's float8_e4m3fn decoding."""
+    import torch
+    from oracle import quant
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = quant.E4M3
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.nanmax(got) == 448.0 and np.nanmin(got[got > 0]) == 2.0 ** -9
+
+
+def test_e4m3_rounding_matches_torch():
+    """Round-to-nearest-even encoding against torch's float32 -> float8
+    conversion on random, tie and subnormal values within +-448."""
+    import torch
+    from oracle import quant
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.uniform(-448, 448, 4000), rng.normal(0, 0.01, 2000),
+                        (quant.E4M3[1:126] + quant.E4M3[2:127]) / 2,          # exact ties
+                        -(quant.E4M3[1:126] + quant.E4M3[2:127]) / 2, [0.0, 448.0, -448.0, 2.0 ** -10]])
+    v = v.astype(np.float32).astype(np.float64)
+    got = quant.encode(v)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch maps -0.0 to code 0x80; the oracle stores zero as +0 (code 0) -- same value
+    bad = (got != ref) & ~((quant.E4M3[got] == 0) & (quant.E4M3[ref] == 0))
+    assert not np.any(bad), v[bad][:5]
+
+
+def test_row_scale_rule():
+    """q = 2^e is the smallest power of two with absmax / q <= 448."""
+    from oracle import quant
+    for a in [1.0, 448.0, 449.0, 1.75, 1.7500001, 3.5, 2.0 ** -20, 1e-3, 123.456, 7.0e4]:
+        e = quant.row_exponent(a)
+        assert a / 2.0 ** e <= 448.0 and a / 2.0 ** (e - 1) > 448.0, (a, e)
+    assert quant.row_exponent(0.0) == 0
+    assert quant.row_exponent(448.0) == 0 and quant.row_exponent(449.0) == 1 and quant.row_exponent(1.0) == -8
+
+
+def test_quantized_rows_error_bound():
+    """Relative error of every element <= 2^-4 (3 mantissa bits, RNE), or
+    absolute <= 2^-10 q in the subnormal range; the row maximum is coded
+    within [224, 448] q."""
+    from oracle import quant
+    rng = np.random.default_rng(5)
+    W = rng.normal(0, 0.02, (64, 300))
+    W[3] = 0.0
+    codes, q = quant.quantize_rows(W)
+    Wq = quant.dequantize(codes, q)
+    err = np.abs(Wq - W)
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(W), 2.0 ** -10 * q[:, None]))
+    assert np.all(Wq[3] == 0) and q[3] == 1.0
+    m = np.max(np.abs(W), axis=1)[np.arange(64) != 3] / q[np.arange(64) != 3]
+    assert np.all((m >= 224.0) & (m <= 448.0))

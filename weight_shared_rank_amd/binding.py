@@ -18,6 +18,7 @@ FAMILIES = ("q", "k", "v", "o", "gate", "up", "down")
 FAMILY = {f: i for i, f in enumerate(FAMILIES)}
 STACKS = {"qkv": 0, "gate_up": 1}
 ACTS = {"gelu_tanh": 0, "silu": 1, "gelu": 2}
+W0_FORMATS = {"bf16": 0, "fp8": 1}
 WL_DTYPE_BF16, WL_DTYPE_F32 = 0, 1
 WL_SRC_W0, WL_SRC_S, WL_SRC_U, WL_SRC_V = 0, 1, 2, 3
 SRC_KIND = {"w0": WL_SRC_W0, "s": WL_SRC_S, "u": WL_SRC_U, "v": WL_SRC_V}
@@ -37,7 +38,8 @@ class WlBundleSpec(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int32), ("num_bands", ctypes.c_int32),
                 ("num_layer_types", ctypes.c_int32), ("layer_type", ctypes.POINTER(ctypes.c_int8)),
                 ("out_dim", (ctypes.c_int32 * 7) * MAX_TYPES), ("in_dim", (ctypes.c_int32 * 7) * MAX_TYPES),
-                ("rank", (ctypes.c_int32 * 7) * MAX_TYPES), ("k_eq_v_type_mask", ctypes.c_uint32)]
+                ("rank", (ctypes.c_int32 * 7) * MAX_TYPES), ("k_eq_v_type_mask", ctypes.c_uint32),
+                ("w0_format", ctypes.c_int32)]
 
 
 class WlSrc(ctypes.Structure):
@@ -97,8 +99,9 @@ def _check(st: int):
 
 def make_spec(num_layers: int, num_bands: int, dims: Dict[Tuple[int, str], Tuple[int, int]],
               ranks: Dict[Tuple[int, str], int], layer_types: Optional[Sequence[int]] = None,
-              k_eq_v_types: Iterable[int] = ()) -> WlBundleSpec:
-    """Spec from Python dicts: dims[(type, family)] = (N, K), ranks[(type, family)] = r."""
+              k_eq_v_types: Iterable[int] = (), w0_format: str = "bf16") -> WlBundleSpec:
+    """Spec from Python dicts: dims[(type, family)] = (N, K), ranks[(type, family)] = r;
+    w0_format "bf16" or "fp8" (E4M3 codes with a power-of-two scale per W0 row)."""
     sp = WlBundleSpec()
     sp.num_layers = num_layers
     sp.num_bands = num_bands
@@ -117,6 +120,7 @@ def make_spec(num_layers: int, num_bands: int, dims: Dict[Tuple[int, str], Tuple
     for t in k_eq_v_types:
         mask |= 1 << t
     sp.k_eq_v_type_mask = mask
+    sp.w0_format = W0_FORMATS[w0_format]
     return sp
 
 

@@ -54,10 +54,17 @@ namespace {
 #ifndef WL_DECODE_TARGET_WGS
 #define WL_DECODE_TARGET_WGS 4096
 #endif
+#ifndef WL_FP8_UNROLL
+#define WL_FP8_UNROLL 2
+#endif
+#ifndef WL_FP8_KS_DIV
+#define WL_FP8_KS_DIV 1
+#endif
 constexpr int kStreamWaves = WL_STREAM_WAVES;
 constexpr int kStreamUnroll = WL_STREAM_UNROLL;
 constexpr int kEpiWaves = WL_EPI_WAVES;
 constexpr int kTargetWgs = WL_DECODE_TARGET_WGS;
+constexpr int kFp8Unroll = WL_FP8_UNROLL;
 
 // One batch of UNROLL complete k-steps (32 k each): loads first, then MFMAs.
 template <int UNROLL>
@@ -78,6 +85,47 @@ __device__ __forceinline__ void kblock(f32x4 &acc, const uint16_t *arow, const u
   for (int j = 0; j < UNROLL; ++j) acc = mfma16x16x32(a[j], b[j], acc);
 }
 
+// 16 E4M3 codes (one 16-byte load) -> two bf16 MFMA fragments: elements
+// 0..7 and 8..15.  v_cvt_scalef32_pk_bf16_fp8 converts two codes per
+// instruction; with scale 1 the result is exact (3 mantissa bits fit in 7).
+__device__ __forceinline__ void fp8x16_to_bf16(u32x4 w, u32x4 &lo, u32x4 &hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, false));
+    o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, true));
+  }
+  lo = u32x4{o[0], o[1], o[2], o[3]};
+  hi = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+// FP8 W0 rows: one 16-byte load per lane covers two 32-k MFMA steps.  Lane
+// group g of pair p holds k = 64p + 16g .. +15; step "lo" takes k 64p + 16g
+// + 0..7 and step "hi" k 64p + 16g + 8..15 (for all four g these are 32
+// distinct k, and x is loaded with the same assignment).
+template <int UNROLL>
+__device__ __forceinline__ void kblock_fp8(f32x4 &acc, const uint8_t *arow, const uint16_t *xrow, bool tok_ok,
+                                           int p0) {
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  u32x4 a[UNROLL], b0[UNROLL], b1[UNROLL];
+#pragma unroll
+  for (int j = 0; j < UNROLL; ++j) a[j] = *reinterpret_cast<const u32x4 *>(arow + (p0 + j) * 64);
+#pragma unroll
+  for (int j = 0; j < UNROLL; ++j) {
+    const u32x4 v0 = ld16(xrow + (p0 + j) * 64), v1 = ld16(xrow + (p0 + j) * 64 + 8);
+    b0[j] = tok_ok ? v0 : zero4;
+    b1[j] = tok_ok ? v1 : zero4;
+  }
+#pragma unroll
+  for (int j = 0; j < UNROLL; ++j) {
+    u32x4 lo, hi;
+    fp8x16_to_bf16(a[j], lo, hi);
+    acc = mfma16x16x32(lo, b0[j], acc);
+    acc = mfma16x16x32(hi, b1[j], acc);
+  }
+}
+
 // 1-D grid: first the V^T tiles (full K, so z needs no summation later; they
 // are dispatched first and finish well inside the launch), then the W0 tiles,
 // each split into KS slices of K.
@@ -91,7 +139,7 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
   const int row0 = (vt ? blockIdx.x : widx / KS) * 16;
   const int slice = vt ? 0 : widx % KS;
   const int nslices = vt ? 1 : KS;
-  const uint16_t *mat = vt ? c.Vt : c.W0;
+  const uint16_t *mat = vt ? c.Vt : c.W0;  // (null for an FP8 bundle's W0 tiles, which read W0f8)
   const int nrows = vt ? c.Rz : c.Ntot;
   const int K = c.K;
   const int nsteps = (K + 31) >> 5;
@@ -101,20 +149,44 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
   // Rows past the end read the tile's first row (always valid); their
   // results are never stored.  Token columns >= T are zero.
   const int arow_idx = (row0 + r16 < nrows) ? row0 + r16 : row0;
-  const uint16_t *arow = mat + static_cast<size_t>(arow_idx) * K + g * 8;
   const bool tok_ok = r16 < c.T;
   const uint16_t *xrow = c.x + static_cast<size_t>(tok_ok ? r16 : 0) * K + g * 8;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int nfull_end = min(s_end, K >> 5);  // steps entirely inside K
-  const int nblocks = max(0, nfull_end - s_begin) / UNROLL;
-  for (int b = wave; b < nblocks; b += W) kblock<UNROLL>(acc, arow, xrow, tok_ok, s_begin + b * UNROLL);
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  for (int s = s_begin + nblocks * UNROLL + wave; s < s_end; s += W) {
-    const bool kin = s * 32 + g * 8 < K;  // the last step may be partial
-    const u32x4 a = kin ? ld16(arow + s * 32) : zero4;
-    const u32x4 v = kin ? ld16(xrow + s * 32) : zero4;
-    acc = mfma16x16x32(a, tok_ok ? v : zero4, acc);
+  if (!vt && c.W0f8) {
+    // FP8 W0: K is walked in pairs of 32-k steps (64 k per 16-byte load);
+    // slices split the pairs.  Codes past K are zero (row padding to ldw0),
+    // x past K is skipped by the per-half guard.
+    const int npairs = (K + 63) >> 6;
+    const int pper = (npairs + KS - 1) / KS;
+    const int p_begin = min(npairs, slice * pper), p_end = min(npairs, p_begin + pper);
+    const uint8_t *arow8 = c.W0f8 + static_cast<size_t>(arow_idx) * c.ldw0 + g * 16;
+    const uint16_t *xrow8 = c.x + static_cast<size_t>(tok_ok ? r16 : 0) * K + g * 16;
+    const int pfull_end = min(p_end, K >> 6);  // pairs entirely inside K
+    const int npb = max(0, pfull_end - p_begin) / kFp8Unroll;
+    for (int b = wave; b < npb; b += W) kblock_fp8<kFp8Unroll>(acc, arow8, xrow8, tok_ok, p_begin + b * kFp8Unroll);
+    for (int pp = p_begin + npb * kFp8Unroll + wave; pp < p_end; pp += W) {
+      const int k0 = pp * 64 + g * 16;
+      const u32x4 a = k0 < c.ldw0 ? *reinterpret_cast<const u32x4 *>(arow8 + pp * 64) : zero4;
+      const u32x4 v0 = k0 < K ? ld16(xrow8 + pp * 64) : zero4;
+      const u32x4 v1 = k0 + 8 < K ? ld16(xrow8 + pp * 64 + 8) : zero4;
+      u32x4 lo, hi;
+      fp8x16_to_bf16(a, lo, hi);
+      acc = mfma16x16x32(lo, tok_ok ? v0 : zero4, acc);
+      acc = mfma16x16x32(hi, tok_ok ? v1 : zero4, acc);
+    }
+  } else {
+    const uint16_t *arow = mat + static_cast<size_t>(arow_idx) * K + g * 8;
+    const int nfull_end = min(s_end, K >> 5);  // steps entirely inside K
+    const int nblocks = max(0, nfull_end - s_begin) / UNROLL;
+    for (int b = wave; b < nblocks; b += W) kblock<UNROLL>(acc, arow, xrow, tok_ok, s_begin + b * UNROLL);
+    for (int s = s_begin + nblocks * UNROLL + wave; s < s_end; s += W) {
+      const bool kin = s * 32 + g * 8 < K;  // the last step may be partial
+      const u32x4 a = kin ? ld16(arow + s * 32) : zero4;
+      const u32x4 v = kin ? ld16(xrow + s * 32) : zero4;
+      acc = mfma16x16x32(a, tok_ok ? v : zero4, acc);
+    }
   }
 
   __shared__ f32x4 red[W][64];
@@ -167,18 +239,22 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
   if (wave == 0 && tok_ok) {
     const size_t sstride = static_cast<size_t>(c.T) * c.Ntot;
     const float *pp = p_part + static_cast<size_t>(r16) * c.Ntot;
-    if (rbase + 3 < c.Ntot && (c.Ntot & 3) == 0 && (reinterpret_cast<uintptr_t>(c.s) & 15) == 0) {
+    // an FP8 bundle's rows carry their W0 scale q too: s q p
+    const float *qrow = c.q;
+    if (rbase + 3 < c.Ntot && (c.Ntot & 3) == 0 &&
+        ((reinterpret_cast<uintptr_t>(c.s) | reinterpret_cast<uintptr_t>(qrow)) & 15) == 0) {
 #pragma unroll
       for (int s = 0; s < kDecodeMaxSlices; ++s)
         part[s] = *reinterpret_cast<const f32x4 *>(pp + static_cast<size_t>(min(s, KS - 1)) * sstride + rbase);
       sc = *reinterpret_cast<const f32x4 *>(c.s + rbase);
+      if (qrow) sc *= *reinterpret_cast<const f32x4 *>(qrow + rbase);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = min(rbase + i, c.Ntot - 1);
 #pragma unroll
         for (int s = 0; s < kDecodeMaxSlices; ++s) part[s][i] = pp[static_cast<size_t>(min(s, KS - 1)) * sstride + row];
-        sc[i] = c.s[row];
+        sc[i] = c.s[row] * (qrow ? qrow[row] : 1.f);
       }
     }
   }
@@ -272,7 +348,7 @@ __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const
 #pragma unroll
         for (int s = 0; s < kDecodeMaxSlices; ++s)
           part[hf][s][i] = pp[static_cast<size_t>(min(s, KS - 1)) * sstride + row];
-        sc[hf][i] = c.s[row];
+        sc[hf][i] = c.s[row] * (c.q ? c.q[row] : 1.f);
       }
   }
 
@@ -341,7 +417,7 @@ int decode_k_slices(int Ntot, int Rz, int K) {
 
 hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream, int act,
                          uint16_t *h, int ldh) {
-  const int KS = decode_k_slices(c.Ntot, c.Rz, c.K);
+  const int KS = c.W0f8 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV) : decode_k_slices(c.Ntot, c.Rz, c.K);
   const int nt_w0 = (c.Ntot + 15) / 16, nt_vt = (c.Rz + 15) / 16;
   hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nt_vt + nt_w0 * KS), dim3(kStreamWaves * 64),
                      0, stream, c, p_part, z_pair, nt_vt, KS);

@@ -32,7 +32,10 @@ struct ChildDesc {
 // One call: rows [0, Ntot) of W0 and s, ranks [0, Rz) of V^T and z.
 struct CallDesc {
   const uint16_t *x;   // [T, K] bf16
-  const uint16_t *W0;  // [Ntot, K] bf16
+  const uint16_t *W0;  // [Ntot, K] bf16 (null for an FP8 bundle's decode call)
+  const uint8_t *W0f8; // FP8 bundle: [Ntot, ldw0] E4M3 codes, else null
+  const float *q;      // FP8 bundle: [Ntot] per-row scale of W0f8, else null
+  int32_t ldw0;        // row stride of W0f8 in bytes
   const float *s;      // [Ntot]
   const uint16_t *Vt;  // [Rz, K] bf16
   uint16_t *y;         // [T, ldy] bf16
@@ -68,6 +71,14 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const 
 hipError_t launch_materialize(const uint16_t *V, const uint16_t *U, int32_t N, int32_t K, int32_t rpad,
                               const float *s, const uint16_t *W0, uint16_t *out, const uint16_t *zero_row,
                               hipStream_t stream);
+
+// FP8 shared block: rows of src bf16 [N][K] -> E4M3 codes dst [N][Kp] (Kp a
+// multiple of 16, padding zero) and per-row power-of-two scales q [N];
+// and back to bf16 [N][K] (value * q).
+hipError_t launch_quantize_rows(const uint16_t *src, int32_t N, int32_t K, uint8_t *dst, int32_t Kp, float *q,
+                                hipStream_t stream);
+hipError_t launch_dequantize_rows(const uint8_t *src, int32_t Kp, const float *q, int32_t N, int32_t K,
+                                  uint16_t *dst, hipStream_t stream);
 
 // Load-time helpers.
 hipError_t launch_fill_zero(void *dst, size_t bytes, hipStream_t stream);

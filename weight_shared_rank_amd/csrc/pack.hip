@@ -1,5 +1,8 @@
 // Load-time kernels used by theta_bundle_load: zero-fill of the arena (so rank
-// padding reads as zero) and the V [K, r] -> V^T [r, K] transpose.
+// padding reads as zero), the V [K, r] -> V^T [r, K] transpose, and the FP8
+// shared block: rows of W0 coded in OCP E4M3 with one power-of-two scale per
+// row (the quantized-shared-block variant, "Quality (Gemma 4 31B)" page,
+// "Verdict"), plus its expansion back to bf16 for the GEMM paths.
 #include "common.h"
 #include "internal.h"
 
@@ -32,7 +35,72 @@ __global__ void transpose_kernel(const uint16_t *V, int K, int r, uint16_t *Vt) 
   }
 }
 
+// One workgroup per W0 row.  e is the smallest integer with
+// max_j |w_j| <= 448 * 2^e (448: largest finite E4M3 value; e = 0 for a zero
+// row); code_j = E4M3(w_j * 2^-e), round to nearest even (the scaling is
+// exact, and |w_j * 2^-e| <= 448 never overflows); q = 2^e.  Bytes K..Kp-1
+// of the row are zero.
+__global__ void quantize_rows_kernel(const uint16_t *src, int K, uint8_t *dst, int Kp, float *q) {
+  const int row = blockIdx.x;
+  const uint16_t *w = src + static_cast<size_t>(row) * K;
+  float m = 0.f;
+  for (int j = threadIdx.x; j < K; j += blockDim.x) m = fmaxf(m, fabsf(bf16_to_f32(w[j])));
+  __shared__ float red[256];
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    if (static_cast<int>(threadIdx.x) < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const float amax = red[0];
+  int e = 0;
+  if (amax > 0.f) {
+    int E;
+    const float f = 2.f * frexpf(amax, &E);  // amax = f * 2^(E-1), f in [1, 2)
+    e = (f <= 1.75f) ? E - 1 - 8 : E - 1 - 7;
+  }
+  uint8_t *d = dst + static_cast<size_t>(row) * Kp;
+  for (int j = 2 * threadIdx.x; j < Kp; j += 2 * blockDim.x) {
+    const float a = j < K ? ldexpf(bf16_to_f32(w[j]), -e) : 0.f;
+    const float b = j + 1 < K ? ldexpf(bf16_to_f32(w[j + 1]), -e) : 0.f;
+    const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    d[j] = static_cast<uint8_t>(packed & 0xff);
+    d[j + 1] = static_cast<uint8_t>((packed >> 8) & 0xff);
+  }
+  if (threadIdx.x == 0) q[row] = ldexpf(1.f, e);
+}
+
+// w[i][j] = E4M3(code) * q[i] as bf16 (exact: 4 significant bits times a
+// power of two), for j < K.
+__global__ void dequantize_rows_kernel(const uint8_t *src, int Kp, const float *q, int K, uint16_t *dst) {
+  const int row = blockIdx.y;
+  const int j = 2 * (blockIdx.x * blockDim.x + threadIdx.x);
+  if (j >= K) return;
+  const uint8_t *s8 = src + static_cast<size_t>(row) * Kp;
+  const uint32_t pair = static_cast<uint32_t>(s8[j]) | (static_cast<uint32_t>(s8[j + 1]) << 8);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(pair), false);
+  const float qv = q[row];
+  uint16_t *d = dst + static_cast<size_t>(row) * K;
+  d[j] = f32_to_bf16(v[0] * qv);
+  d[j + 1] = f32_to_bf16(v[1] * qv);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t *src, int32_t N, int32_t K, uint8_t *dst, int32_t Kp, float *q,
+                                hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3(N), dim3(256), 0, stream, src, K, dst, Kp, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_rows(const uint8_t *src, int32_t Kp, const float *q, int32_t N, int32_t K,
+                                  uint16_t *dst, hipStream_t stream) {
+  if (N == 0 || K == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequantize_rows_kernel, dim3((K / 2 + 255) / 256, N), dim3(256), 0, stream, src, Kp, q, K, dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(void *dst, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return hipSuccess;

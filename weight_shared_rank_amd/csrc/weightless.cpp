@@ -70,6 +70,7 @@ struct GroupShape {
   bool any = false;
   bool tied = false;  // QKV group on a K=V-tied type: the v slot copies k
   int K = 0;
+  int Kp = 0;         // FP8 W0 row stride in bytes (K rounded up to 16)
   int nchild = 0;
   int fam[3] = {-1, -1, -1};
   int N[3] = {0, 0, 0};
@@ -94,6 +95,8 @@ struct Layout {
   uint32_t tied_mask = 0;
   GroupShape gs[WL_MAX_LAYER_TYPES][kGroups];
   std::vector<int64_t> w0;  // [(band * NT + tkey) * kGroups + g], -1 if absent
+  std::vector<int64_t> w0q; // FP8 bundles: per-row scales of that W0 block
+  bool fp8 = false;
   std::vector<LayerOff> lay;
   size_t bytes = 0;
   size_t zero_off = 0;  // 256 zero bytes
@@ -103,6 +106,9 @@ struct Layout {
   int band(int l) const { return static_cast<int>((static_cast<int64_t>(l) * G) / L); }
   int64_t &w0_at(int b, int t, int g) { return w0[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
   int64_t w0_at(int b, int t, int g) const { return w0[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
+  int64_t &w0q_at(int b, int t, int g) { return w0q[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
+  int64_t w0q_at(int b, int t, int g) const { return w0q[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
+  size_t w0_row_bytes(const GroupShape &gs) const { return fp8 ? static_cast<size_t>(gs.Kp) : static_cast<size_t>(gs.K) * 2; }
 };
 
 bool tied(const Layout &lo, int t) { return (lo.tied_mask >> t) & 1u; }
@@ -115,6 +121,9 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
   if (G < 1 || G > L) return fail(WL_EINVAL, "num_bands %d must be in [1, num_layers=%d]", G, L);
   if (NT < 1 || NT > WL_MAX_LAYER_TYPES) return fail(WL_EINVAL, "num_layer_types %d must be 1 or 2", NT);
   if (spec->k_eq_v_type_mask >> NT) return fail(WL_EINVAL, "k_eq_v_type_mask 0x%x names a layer type >= %d", spec->k_eq_v_type_mask, NT);
+  if (spec->w0_format != WL_W0_BF16 && spec->w0_format != WL_W0_FP8)
+    return fail(WL_EINVAL, "w0_format %d invalid", spec->w0_format);
+  lo.fp8 = spec->w0_format == WL_W0_FP8;
   lo.L = L;
   lo.G = G;
   lo.NT = NT;
@@ -165,6 +174,7 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
           return fail(WL_ESHAPE, "families of one stacked group need one in_dim (type %d family %d: %d vs %d)", t, f, K, gs.K);
         const int c = gs.nchild++;
         gs.K = K;
+        gs.Kp = (K + 15) & ~15;
         gs.fam[c] = f;
         gs.N[c] = N;
         gs.r[c] = spec->rank[t][f];
@@ -184,6 +194,7 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
   // W0 regions: one per (band, type key, group) used by some layer.
   size_t off = 0;
   lo.w0.assign(static_cast<size_t>(G) * NT * kGroups, -1);
+  lo.w0q.assign(static_cast<size_t>(G) * NT * kGroups, -1);
   for (int b = 0; b < G; ++b) {
     for (int t = 0; t < NT; ++t) {
       for (int g = 0; g < kGroups; ++g) {
@@ -194,7 +205,11 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
         if (!used) continue;
         const GroupShape &gs = lo.gs[t][g];
         lo.w0_at(b, t, g) = static_cast<int64_t>(off);
-        off = align256(off + static_cast<size_t>(gs.Ntot) * gs.K * 2);
+        off = align256(off + static_cast<size_t>(gs.Ntot) * lo.w0_row_bytes(gs));
+        if (lo.fp8) {
+          lo.w0q_at(b, t, g) = static_cast<int64_t>(off);
+          off = align256(off + static_cast<size_t>(gs.Ntot) * 4);
+        }
       }
     }
   }
@@ -251,12 +266,25 @@ size_t ws_prefill_partial_bytes(const Layout &lo, int32_t T) {
   return align256(n);
 }
 
+// FP8 bundles: the bf16 expansion of the largest W0 row block a call reads
+// (prefill and materialization run the bf16 GEMM on it).
+size_t ws_w0_expand_bytes(const Layout &lo) {
+  if (!lo.fp8) return 0;
+  size_t n = 0;
+  for (int t = 0; t < lo.NT; ++t)
+    for (int g = 0; g < kGroups; ++g) {
+      const GroupShape &gs = lo.gs[t][g];
+      if (gs.any) n = std::max(n, static_cast<size_t>(gs.Ntot) * gs.K * 2);
+    }
+  return align256(n);
+}
+
 size_t ws_bytes_for(const Layout &lo, int32_t T) {
   size_t n;
   if (T <= wl::kDecodeMaxT)
     n = ws_p_part_bytes(lo, T) + align256(static_cast<size_t>(T) * lo.Rmax * 4);
   else
-    n = ws_prefill_z_bytes(lo, T) + ws_prefill_partial_bytes(lo, T);
+    n = ws_prefill_z_bytes(lo, T) + ws_prefill_partial_bytes(lo, T) + ws_w0_expand_bytes(lo);
   return n < 256 ? 256 : n;
 }
 
@@ -314,7 +342,14 @@ wl_status resolve(const wl_bundle *h, int32_t layer, int32_t family, int32_t sta
   const int rs0 = gs.row_start[first];
   const int z0 = gs.zoff[first];
   c.K = gs.K;
-  c.W0 = reinterpret_cast<const uint16_t *>(A + w0off) + static_cast<size_t>(rs0) * gs.K;
+  if (lo.fp8) {
+    c.W0 = nullptr;
+    c.W0f8 = A + w0off + static_cast<size_t>(rs0) * gs.Kp;
+    c.q = reinterpret_cast<const float *>(A + lo.w0q_at(b, tkey, g)) + rs0;
+    c.ldw0 = gs.Kp;
+  } else {
+    c.W0 = reinterpret_cast<const uint16_t *>(A + w0off) + static_cast<size_t>(rs0) * gs.K;
+  }
   c.s = reinterpret_cast<const float *>(A + lf.s[g]) + rs0;
   c.Vt = reinterpret_cast<const uint16_t *>(A + lf.vt[g]) + static_cast<size_t>(z0) * gs.K;
   c.nchild = last - first;
@@ -387,6 +422,13 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
     for (int c = 0; c < rv.c.nchild; ++c) rmax = std::max(rmax, static_cast<int>(rv.c.ch[c].rpad));
     if (wl::prefill_partial_bytes(rv.c.Ntot, rv.c.Rz, rmax, rv.c.K, T) > ws_prefill_partial_bytes(h->lo, T))
       return fail(WL_ENOSPACE, "internal: prefill partials of this call exceed the planned workspace");
+    if (h->lo.fp8) {
+      // FP8 bundle: expand this call's W0 rows to bf16 for the GEMM
+      uint16_t *w0 = reinterpret_cast<uint16_t *>(ws + ws_prefill_z_bytes(h->lo, T) + ws_prefill_partial_bytes(h->lo, T));
+      e = wl::launch_dequantize_rows(rv.c.W0f8, rv.c.ldw0, rv.c.q, rv.c.Ntot, rv.c.K, w0, s);
+      if (e != hipSuccess) return hip_fail(e, "W0 expand launch");
+      rv.c.W0 = w0;
+    }
     e = wl::launch_prefill(rv.c, reinterpret_cast<uint16_t *>(ws),
                            reinterpret_cast<float *>(ws + ws_prefill_z_bytes(h->lo, T)),
                            reinterpret_cast<const uint16_t *>(h->arena + h->lo.zero_off), s, act, hout,
@@ -460,6 +502,8 @@ wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size
       return fail(WL_EINVAL, "source %zu (kind %d, index %d, type %d, family %d) is not part of this bundle", i, s.kind,
                   s.index, s.layer_type, s.family);
     if (it->second >= 0) return fail(WL_EINVAL, "source %zu duplicates source %d", i, it->second);
+    if (s.kind == WL_SRC_W0 && lo.fp8 && !s.on_device)
+      return fail(WL_EINVAL, "source %zu: an FP8 bundle codes W0 on the device; pass a device tensor", i);
     it->second = static_cast<int>(i);
   }
   for (const auto &kv : expect)
@@ -482,7 +526,13 @@ wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size
       const int g = kGroupOf[s.family];
       const GroupShape &gs = lo.gs[t][g];
       const int c = gs.child_of_fam[s.family];
-      uint8_t *dst = A + lo.w0_at(s.index, t, g) + static_cast<size_t>(gs.row_start[c]) * gs.K * 2;
+      uint8_t *dst = A + lo.w0_at(s.index, t, g) + static_cast<size_t>(gs.row_start[c]) * lo.w0_row_bytes(gs);
+      if (lo.fp8) {
+        float *q = reinterpret_cast<float *>(A + lo.w0q_at(s.index, t, g)) + gs.row_start[c];
+        e = wl::launch_quantize_rows(static_cast<const uint16_t *>(s.ptr), gs.N[c], gs.K, dst, gs.Kp, q, strm);
+        if (e != hipSuccess) return hip_fail(e, "W0 quantize");
+        continue;
+      }
       e = hipMemcpyAsync(dst, s.ptr, static_cast<size_t>(gs.N[c]) * gs.K * 2, kind, strm);
       if (e != hipSuccess) return hip_fail(e, "W0 copy");
       continue;
@@ -578,7 +628,7 @@ size_t weightless_materialize_workspace_bytes(const wl_bundle *bundle) {
       for (int c = 0; c < gs.nchild; ++c)
         n = std::max(n, align256(static_cast<size_t>(gs.K) * gs.rpad[c] * 2));
     }
-  return n;
+  return n + ws_w0_expand_bytes(lo);
 }
 
 wl_status weightless_materialize(const wl_bundle *bundle, int32_t layer, int32_t family, void *d_weff, void *d_ws,
@@ -602,7 +652,14 @@ wl_status weightless_materialize(const wl_bundle *bundle, int32_t layer, int32_t
   // V^T [rpad][K] -> V rows [K][rpad] (ranks contiguous), the GEMM's A operand
   hipError_t e = wl::launch_transpose_v(c.Vt, ch.rpad, c.K, vrows, s);
   if (e != hipSuccess) return hip_fail(e, "transpose launch");
-  e = wl::launch_materialize(vrows, ch.U, c.Ntot, c.K, ch.rpad, c.s, c.W0, static_cast<uint16_t *>(d_weff),
+  const uint16_t *w0 = c.W0;
+  if (bundle->lo.fp8) {
+    uint16_t *buf = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(d_ws) + need - ws_w0_expand_bytes(bundle->lo));
+    e = wl::launch_dequantize_rows(c.W0f8, c.ldw0, c.q, c.Ntot, c.K, buf, s);
+    if (e != hipSuccess) return hip_fail(e, "W0 expand launch");
+    w0 = buf;
+  }
+  e = wl::launch_materialize(vrows, ch.U, c.Ntot, c.K, ch.rpad, c.s, w0, static_cast<uint16_t *>(d_weff),
                              reinterpret_cast<const uint16_t *>(bundle->arena + bundle->lo.zero_off), s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return WL_OK;
