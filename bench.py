@@ -375,9 +375,17 @@ def cpu_baseline(wl, T, budget_s, dev):
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 5000:
             break
+    blas = "unknown BLAS"
+    try:
+        import threadpoolctl
+        libs = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
     return {"value": nbytes * n / el / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 numpy oracle, layer 0 of the headline workload (4 calls, {nbytes/1e9:.3f} GB of "
-                      f"bundle bytes), repeated {n}x in {el:.1f} s; W0/s/U/V pre-upcast to fp64 outside the timing"}
+            "sample": f"fp64 numpy oracle ({blas}), layer 0 of the headline workload (4 calls, {nbytes/1e9:.3f} GB "
+                      f"of bundle bytes), repeated {n}x in {el:.1f} s; W0/s/U/V pre-upcast to fp64 outside the timing"}
 
 
 def band_reuse(dev, reps=5):

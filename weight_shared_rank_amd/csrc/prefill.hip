@@ -314,7 +314,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
         if (nv == 4 && ((a.M | row) & 3) == 0) {
           *reinterpret_cast<f32x4 *>(prow + row) = acc[i][j];
         } else {
-          for (int e = 0; e < nv; ++e) prow[row + e] = acc[i][j][e];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < nv) prow[row + e] = acc[i][j][e];
         }
       }
     }
@@ -352,7 +354,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
           *reinterpret_cast<uint2 *>(hrow + jj) =
               make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
         } else {
-          for (int e = 0; e < nv; ++e) hrow[jj + e] = o[e];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < nv) hrow[jj + e] = o[e];
         }
       }
     }
@@ -387,10 +391,14 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
           *reinterpret_cast<uint2 *>(yrow + row) =
               make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
         } else {
-          for (int e = 0; e < nv; ++e) yrow[row + e] = o[e];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < nv) yrow[row + e] = o[e];
         }
       } else {
-        for (int e = 0; e < nv; ++e) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (e >= nv) break;
           const int r = row + e;
           int ci = 0;
           while (ci + 1 < a.nchild && r >= a.ch[ci + 1].row_start) ++ci;
