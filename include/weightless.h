@@ -206,6 +206,41 @@ size_t weightless_materialize_workspace_bytes(const wl_bundle *bundle);
 wl_status weightless_materialize(const wl_bundle *bundle, int32_t layer, int32_t family, void *d_weff,
                                  void *d_ws, size_t ws_bytes, void *stream);
 
+/* ---- Decomposition ("Add a new model architecture" page, "Decompose HF
+ * weights"; "Quality" page, "Why sharing fails: reconstruction error") ----
+ * The analytic one-shot decomposition of one band of one family, on the GPU:
+ *   W0 = bf16(mean of the band's m layers), the mean taken in fp64;
+ *   per layer, s_i = <W_i, W0_i> / <W0_i, W0_i> (1 for a zero row of W0),
+ *   computed in fp64 against the rounded W0 and stored fp32;
+ *   U V^T = rank-r truncated SVD of R = W - diag(s) W0, split as
+ *   U = P sqrt(S), V = Q sqrt(S), stored bf16.
+ * The SVD is randomized subspace iteration (Halko, Martinsson and Tropp,
+ * 2011): l = min(rank + oversample, N, K) sketch columns, power_iters rounds,
+ * fp32 GPU products, Cholesky-QR twice for each orthonormalization and a
+ * Jacobi eigen-solve of the l x l Gram matrix on the host.  Its delta is the
+ * exact truncated SVD's up to the sketch's accuracy: the error approaches
+ * Eckart-Young's as power_iters grows and is exact when rank(R) <= l.
+ *
+ * Workspace bytes for one call (fp32 residual, sketches and factors); 0 if
+ * an argument is out of range. */
+size_t weightless_decompose_workspace_bytes(int32_t N, int32_t K, int32_t rank, int32_t oversample);
+
+/* d_w: bf16 [m][N][K], the band's layers in layer order (device).
+ * d_omega: fp32 [K][l] test matrix, l = min(rank + oversample, N, K)
+ *   (device; the caller draws it, e.g. standard normal; may be NULL if
+ *   rank == 0).
+ * Outputs (device): d_w0 bf16 [N][K]; d_s fp32 [m][N]; d_u bf16 [m][N][rank];
+ *   d_v bf16 [m][K][rank] (the layouts theta_bundle_load takes; d_u, d_v may
+ *   be NULL if rank == 0).  A zero residual gives U = V = 0.
+ * d_ws: >= weightless_decompose_workspace_bytes(N, K, rank, oversample)
+ *   bytes, 256-byte aligned.
+ * Runs on `stream` and synchronizes it several times per layer (the small
+ * host steps); returns when the outputs are written.  WL_EINVAL for NULL
+ * pointers, bad counts or non-finite weights; WL_ESHAPE if rank > min(N, K). */
+wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K, int32_t rank, int32_t oversample,
+                               int32_t power_iters, const float *d_omega, void *d_w0, float *d_s, void *d_u,
+                               void *d_v, void *d_ws, size_t ws_bytes, void *stream);
+
 /* Output width N of a single-family call, or of a stacked call (stack >= 0
  * with family < 0); 0 on error.  Host-only. */
 int32_t weightless_out_dim(const wl_bundle *bundle, int32_t layer, int32_t family, int32_t stack);

@@ -37,7 +37,7 @@ MLP_FAMILIES = ("gate", "up", "down")
 # Calls a decoder layer makes, in order: (call name, families in output order).
 CALLS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
 
-_KIND = {"w0": 1, "s": 2, "u": 3, "v": 4, "x": 5, "layer_w": 6}
+_KIND = {"w0": 1, "s": 2, "u": 3, "v": 4, "x": 5, "layer_w": 6, "band_w": 7, "sketch": 8}
 
 
 def _seed(root: int, kind: str, index: int, ltype: int, fam: int, extra: int = 0) -> int:
@@ -199,3 +199,32 @@ def custom(num_layers: int, num_bands: int, rank: int, dims, layer_types=None,
     lt = tuple(layer_types) if layer_types is not None else (0,) * num_layers
     return Workload(cid, "custom", num_layers, num_bands, rank, (1,), dict(dims), lt,
                     tuple(k_eq_v_types), x_std=x_std)
+
+
+def band_layers(seed: int, m: int, N: int, K: int, planted_rank: int = 0, planted_std: float = 1.0,
+                device="cpu") -> torch.Tensor:
+    """Per-layer weights of one band, bf16 [m, N, K]: the input of a
+    decomposition.  planted_rank == 0: each layer i.i.d. N(0, 1/K), the
+    distribution the oracle workloads decompose.  planted_rank = p > 0: a
+    block B shared by all layers plus, per layer, a rank-p part P_l Q_l^T
+    (P ~ N(0, planted_std^2 / K), Q ~ N(0, 1), so its entries are about
+    planted_std * sqrt(p / K)) and no other per-layer term; the layers then
+    differ from their mean by a matrix of rank <= m p, a spectrum with a gap.
+    The planted product is how the input is drawn, not a step of the method."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(_seed(seed, "band_w", m, N, K, planted_rank))
+    std = 1.0 / math.sqrt(K)
+    if planted_rank == 0:
+        w = torch.randn((m, N, K), generator=g, dtype=torch.float32) * std
+    else:
+        base = torch.randn((N, K), generator=g, dtype=torch.float32) * std
+        P = torch.randn((m, N, planted_rank), generator=g, dtype=torch.float32) * (planted_std * std)
+        Q = torch.randn((m, K, planted_rank), generator=g, dtype=torch.float32)
+        w = base.unsqueeze(0) + torch.bmm(P, Q.transpose(1, 2).contiguous())
+    return w.to(torch.bfloat16).to(device)
+
+
+def sketch_matrix(seed: int, K: int, cols: int, device="cpu") -> torch.Tensor:
+    """Standard normal fp32 [K, cols] test matrix for a randomized range finder
+    (drawn on the CPU, then moved, so every device gets the same values)."""
+    return _normal((K, cols), _seed(seed, "sketch", K, cols, 0), 0.0, 1.0, "cpu").to(device)

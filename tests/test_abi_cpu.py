@@ -221,3 +221,31 @@ def test_fp8_spec_and_sources(L):
     h = ctypes.c_void_p()
     assert L.theta_bundle_load(ctypes.byref(sp8), srcs, 1, FAKE_ARENA, n8, None, ctypes.byref(h)) == -1
     assert "device" in binding.last_error()
+
+
+def test_decompose_workspace_and_argument_errors(L):
+    """weightless_decompose: workspace sizing, and every argument error is
+    reported before any HIP call."""
+    ws = L.weightless_decompose_workspace_bytes(4096, 1152, 32, 8)
+    # fp32 residual + 2 (N x l) + 2 (K x l) + (l x K) + (l x l) + max(N, K) x r, l = 40
+    expect = 4 * (4096 * 1152 + 2 * 4096 * 40 + 2 * 1152 * 40 + 40 * 1152 + 40 * 40 + 4096 * 32)
+    assert expect <= ws <= expect + 8 * 256
+    assert L.weightless_decompose_workspace_bytes(0, 8, 1, 0) == 0
+    assert L.weightless_decompose_workspace_bytes(8, 8, -1, 0) == 0
+    assert binding.sketch_columns(100, 64, 60, 8) == 64
+    big = 1 << 30
+    args = dict(w=FAKE_ARENA, m=2, N=64, K=48, rank=8, over=4, q=2, omega=FAKE_ARENA, w0=FAKE_ARENA,
+                s=FAKE_ARENA, u=FAKE_ARENA, v=FAKE_ARENA, ws=FAKE_ARENA, wsb=big)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.weightless_decompose(a["w"], a["m"], a["N"], a["K"], a["rank"], a["over"], a["q"], a["omega"],
+                                      a["w0"], a["s"], a["u"], a["v"], a["ws"], a["wsb"], None)
+
+    assert call(rank=49) == -2 and "rank" in binding.last_error()
+    assert call(m=0) == -1
+    assert call(q=17) == -1
+    assert call(w=None) == -1 and "NULL" in binding.last_error()
+    assert call(omega=None) == -1
+    assert call(ws=FAKE_ARENA + 16) == -1 and "aligned" in binding.last_error()
+    assert call(wsb=1024) == -5

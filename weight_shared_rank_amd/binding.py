@@ -31,7 +31,8 @@ DECODE_MAX_T = 16
 EXPORTS = ("theta_bundle_arena_bytes", "theta_bundle_load", "theta_bundle_free",
            "weightless_workspace_bytes",
            "weightless_linear", "weightless_stacked_linear", "weightless_out_dim", "wl_last_error",
-           "weightless_materialize_workspace_bytes", "weightless_materialize", "weightless_gate_up_act")
+           "weightless_materialize_workspace_bytes", "weightless_materialize", "weightless_gate_up_act",
+           "weightless_decompose_workspace_bytes", "weightless_decompose")
 
 
 class WlBundleSpec(ctypes.Structure):
@@ -79,6 +80,8 @@ def lib():
         "weightless_materialize_workspace_bytes": (sz, [vp]),
         "weightless_materialize": (i32, [vp, i32, i32, vp, vp, sz, vp]),
         "weightless_gate_up_act": (i32, [vp, i32, i32, vp, i32, vp, vp, sz, vp]),
+        "weightless_decompose_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "weightless_decompose": (i32, [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -256,3 +259,40 @@ class ThetaBundle:
         _check(lib().weightless_materialize(self.handle, layer, FAMILY[family], out.data_ptr(), ws.data_ptr(),
                                             ws.numel(), _stream_ptr(stream)))
         return out
+
+
+def sketch_columns(N: int, K: int, rank: int, oversample: int) -> int:
+    """Columns l of the test matrix weightless_decompose takes: min(rank + oversample, N, K)."""
+    return min(rank + oversample, N, K)
+
+
+def decompose(w, rank: int, omega=None, oversample: int = 16, power_iters: int = 4, stream=None):
+    """Decompose one band of one family on the GPU.
+
+    w: bf16 [m, N, K] device tensor (the band's layers in layer order);
+    omega: fp32 [K, l] device test matrix, l = sketch_columns(N, K, rank, oversample)
+    (required when rank > 0).  Returns (W0 bf16 [N, K], s fp32 [m, N],
+    U bf16 [m, N, rank], V bf16 [m, K, rank]), the layouts theta_bundle_load takes."""
+    import torch
+    if w.dim() != 3 or w.dtype != torch.bfloat16 or not w.is_cuda or not w.is_contiguous():
+        raise WlError(-1, "w must be a contiguous bf16 [m, N, K] device tensor")
+    m, n, k = w.shape
+    dev = w.device
+    l = sketch_columns(n, k, rank, oversample)
+    if rank > 0:
+        if omega is None or tuple(omega.shape) != (k, l) or omega.dtype != torch.float32 \
+                or not omega.is_contiguous() or omega.device != dev:
+            raise WlError(-1, f"omega must be a contiguous fp32 [{k}, {l}] tensor on {dev}")
+    need = lib().weightless_decompose_workspace_bytes(n, k, rank, oversample)
+    if need == 0:
+        raise WlError(-1, "weightless_decompose_workspace_bytes: arguments out of range")
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    w0 = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+    s = torch.empty((m, n), dtype=torch.float32, device=dev)
+    u = torch.empty((m, n, rank), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((m, k, rank), dtype=torch.bfloat16, device=dev)
+    _check(lib().weightless_decompose(w.data_ptr(), m, n, k, rank, oversample, power_iters,
+                                      omega.data_ptr() if rank > 0 else None, w0.data_ptr(), s.data_ptr(),
+                                      u.data_ptr() if rank > 0 else None, v.data_ptr() if rank > 0 else None,
+                                      ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
+    return w0, s, u, v

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libweightless.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["weightless.cpp", "decode.hip", "prefill.hip", "pack.hip"]
+SOURCES = ["weightless.cpp", "decode.hip", "prefill.hip", "pack.hip", "decompose_kernels.hip", "decompose.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-x", "hip",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function",

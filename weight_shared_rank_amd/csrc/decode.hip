@@ -89,7 +89,6 @@ __device__ __forceinline__ void kblock(f32x4 &acc, const uint16_t *arow, const u
 // 0..7 and 8..15.  v_cvt_scalef32_pk_bf16_fp8 converts two codes per
 // instruction; with scale 1 the result is exact (3 mantissa bits fit in 7).
 __device__ __forceinline__ void fp8x16_to_bf16(u32x4 w, u32x4 &lo, u32x4 &hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

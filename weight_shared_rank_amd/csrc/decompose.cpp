@@ -1,0 +1,276 @@
+// GPU decomposition of one band of one family into a theta bundle: the band
+// mean W0, per layer the least-squares row scale s and the rank-r delta U V^T
+// of the residual ("Add a new model architecture" page, "Decompose HF
+// weights"; readings as in the oracle: contiguous bands, LS scale, symmetric
+// sqrt(S) split, bf16 storage with W0 rounded before s is fitted).
+//
+// The truncated SVD of each residual R [N, K] is randomized subspace
+// iteration (Halko, Martinsson and Tropp, "Finding structure with
+// randomness", 2011): Y = R Omega with l = r + p columns, q rounds of
+// Z = R^T Y, Y = R Z, each product orthonormalized by Cholesky-QR done twice;
+// then B = Q^T R, the small symmetric eigenproblem B B^T = W Lambda W^T on
+// the host in double (cyclic Jacobi), sigma = sqrt(Lambda), U = Q W_r
+// sqrt(sigma_r), V = B^T W_r / sqrt(sigma_r).  The products run on the GPU in
+// fp32; the host sees only l x l matrices.  The test matrix Omega is the
+// caller's (random numbers are inputs).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+#include "weightless.h"
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// In-place Cholesky A = L L^T of a symmetric positive-definite n x n matrix
+// (row-major, lower triangle written); false if a pivot is not positive.
+bool cholesky(std::vector<double> &a, int n) {
+  for (int j = 0; j < n; ++j) {
+    double d = a[j * n + j];
+    for (int k = 0; k < j; ++k) d -= a[j * n + k] * a[j * n + k];
+    if (!(d > 0.0)) return false;
+    const double ljj = std::sqrt(d);
+    a[j * n + j] = ljj;
+    for (int i = j + 1; i < n; ++i) {
+      double v = a[i * n + j];
+      for (int k = 0; k < j; ++k) v -= a[i * n + k] * a[j * n + k];
+      a[i * n + j] = v / ljj;
+    }
+  }
+  return true;
+}
+
+// T = L^{-T} (upper triangular), row-major n x n, from the lower factor L.
+std::vector<double> inv_lower_transpose(const std::vector<double> &L, int n) {
+  // X = L^{-1} (lower) by forward substitution, then T = X^T
+  std::vector<double> X(static_cast<size_t>(n) * n, 0.0);
+  for (int c = 0; c < n; ++c) {
+    for (int i = c; i < n; ++i) {
+      double v = (i == c) ? 1.0 : 0.0;
+      for (int k = c; k < i; ++k) v -= L[i * n + k] * X[k * n + c];
+      X[i * n + c] = v / L[i * n + i];
+    }
+  }
+  std::vector<double> T(static_cast<size_t>(n) * n, 0.0);
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) T[i * n + j] = X[j * n + i];
+  return T;
+}
+
+// Cyclic Jacobi eigen-decomposition of a symmetric n x n matrix (row-major):
+// eigenvalues descending in lam, eigenvectors as columns of V.
+void jacobi_eigen(std::vector<double> a, int n, std::vector<double> &lam, std::vector<double> &V) {
+  V.assign(static_cast<size_t>(n) * n, 0.0);
+  for (int i = 0; i < n; ++i) V[i * n + i] = 1.0;
+  for (int sweep = 0; sweep < 100; ++sweep) {
+    double off = 0.0, tot = 0.0;
+    for (int i = 0; i < n; ++i)
+      for (int j = 0; j < n; ++j) {
+        tot += a[i * n + j] * a[i * n + j];
+        if (i != j) off += a[i * n + j] * a[i * n + j];
+      }
+    if (off <= 1e-30 * tot || off == 0.0) break;
+    for (int p = 0; p < n; ++p)
+      for (int q = p + 1; q < n; ++q) {
+        const double apq = a[p * n + q];
+        if (apq == 0.0) continue;
+        const double theta = (a[q * n + q] - a[p * n + p]) / (2.0 * apq);
+        const double t = (theta >= 0 ? 1.0 : -1.0) / (std::fabs(theta) + std::sqrt(theta * theta + 1.0));
+        const double c = 1.0 / std::sqrt(t * t + 1.0), s = t * c;
+        for (int k = 0; k < n; ++k) {  // rotate columns p, q
+          const double akp = a[k * n + p], akq = a[k * n + q];
+          a[k * n + p] = c * akp - s * akq;
+          a[k * n + q] = s * akp + c * akq;
+        }
+        for (int k = 0; k < n; ++k) {  // rotate rows p, q
+          const double apk = a[p * n + k], aqk = a[q * n + k];
+          a[p * n + k] = c * apk - s * aqk;
+          a[q * n + k] = s * apk + c * aqk;
+        }
+        for (int k = 0; k < n; ++k) {
+          const double vkp = V[k * n + p], vkq = V[k * n + q];
+          V[k * n + p] = c * vkp - s * vkq;
+          V[k * n + q] = s * vkp + c * vkq;
+        }
+      }
+  }
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::sort(order.begin(), order.end(), [&](int x, int y) { return a[x * n + x] > a[y * n + y]; });
+  lam.resize(n);
+  std::vector<double> Vs(static_cast<size_t>(n) * n);
+  for (int c = 0; c < n; ++c) {
+    lam[c] = a[order[c] * n + order[c]];
+    for (int k = 0; k < n; ++k) Vs[k * n + c] = V[k * n + order[c]];
+  }
+  V.swap(Vs);
+}
+
+struct Dev {
+  hipStream_t s;
+  hipError_t err = hipSuccess;
+  bool ok() const { return err == hipSuccess; }
+  void put(float *d, const std::vector<double> &h) {
+    if (!ok()) return;
+    std::vector<float> f(h.begin(), h.end());
+    err = hipMemcpyAsync(d, f.data(), f.size() * 4, hipMemcpyHostToDevice, s);
+    if (ok()) err = hipStreamSynchronize(s);
+  }
+  std::vector<double> get(const float *d, size_t n) {
+    std::vector<float> f(n);
+    if (ok()) err = hipMemcpyAsync(f.data(), d, n * 4, hipMemcpyDeviceToHost, s);
+    if (ok()) err = hipStreamSynchronize(s);
+    return std::vector<double>(f.begin(), f.end());
+  }
+};
+
+// Y [n x l] <- Y T with Y^T Y = L L^T and T = L^-T, done twice (CholQR2).
+// A rank-deficient Y gets a small diagonal shift before the first factoring
+// (shifted Cholesky-QR); tmp is another n x l buffer.
+enum Orth { kOrthOk, kOrthZero, kOrthFail };
+Orth orthonormalize(Dev &d, float *&Y, float *&tmp, int n, int l, float *small) {
+  for (int pass = 0; pass < 2 && d.ok(); ++pass) {
+    d.err = wl::launch_gemm_f32(Y, 1, l, Y, l, 1, small, l, l, l, n, d.s);  // G = Y^T Y
+    std::vector<double> G = d.get(small, static_cast<size_t>(l) * l);
+    if (!d.ok()) return kOrthFail;
+    double tr = 0.0;
+    for (int i = 0; i < l; ++i) tr += G[i * l + i];
+    if (tr == 0.0) return kOrthZero;
+    if (!std::isfinite(tr)) return kOrthFail;
+    std::vector<double> L = G;
+    bool good = cholesky(L, l);
+    for (int attempt = 0; !good && attempt < 6; ++attempt) {
+      L = G;
+      const double shift = tr / l * std::pow(10.0, -7 + attempt);
+      for (int i = 0; i < l; ++i) L[i * l + i] += shift;
+      good = cholesky(L, l);
+    }
+    if (!good) return kOrthFail;
+    d.put(small, inv_lower_transpose(L, l));
+    if (d.ok()) d.err = wl::launch_gemm_f32(Y, l, 1, small, l, 1, tmp, l, n, l, l, d.s);  // Y T
+    std::swap(Y, tmp);
+  }
+  return d.ok() ? kOrthOk : kOrthFail;
+}
+
+wl_status report(wl_status st, const char *what, int layer, hipError_t e) {
+  char buf[256];
+  if (st == WL_EHIP)
+    std::snprintf(buf, sizeof buf, "weightless_decompose: layer %d: %s", layer, hipGetErrorString(e));
+  else
+    std::snprintf(buf, sizeof buf, "weightless_decompose: layer %d: %s", layer, what);
+  wl::set_last_error(buf);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t weightless_decompose_workspace_bytes(int32_t N, int32_t K, int32_t rank, int32_t oversample) {
+  if (N <= 0 || K <= 0 || rank < 0 || oversample < 0) return 0;
+  const size_t l = static_cast<size_t>(std::min<int64_t>(static_cast<int64_t>(rank) + oversample, std::min(N, K)));
+  size_t n = align256(static_cast<size_t>(N) * K * 4);        // R
+  n += 2 * align256(static_cast<size_t>(N) * l * 4);          // Y, spare
+  n += 2 * align256(static_cast<size_t>(K) * l * 4);          // Z, spare
+  n += align256(l * K * 4);                                   // B
+  n += align256(l * l * 4);                                   // small
+  n += align256(static_cast<size_t>(std::max(N, K)) * rank * 4);  // U or V in fp32
+  return n;
+}
+
+wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K, int32_t rank, int32_t oversample,
+                               int32_t power_iters, const float *d_omega, void *d_w0, float *d_s, void *d_u,
+                               void *d_v, void *d_ws, size_t ws_bytes, void *stream) {
+  if (m < 1 || N < 1 || K < 1 || rank < 0 || oversample < 0 || power_iters < 0 || power_iters > 16)
+    return report(WL_EINVAL, "need m, N, K >= 1, rank, oversample >= 0 and 0 <= power_iters <= 16", -1, hipSuccess);
+  if (rank > std::min(N, K)) return report(WL_ESHAPE, "rank exceeds min(N, K)", -1, hipSuccess);
+  if (!d_w || !d_w0 || !d_s || !d_ws || (rank > 0 && (!d_u || !d_v || !d_omega)))
+    return report(WL_EINVAL, "NULL pointer", -1, hipSuccess);
+  if (reinterpret_cast<uintptr_t>(d_ws) % 256) return report(WL_EINVAL, "workspace not 256-byte aligned", -1, hipSuccess);
+  if (ws_bytes < weightless_decompose_workspace_bytes(N, K, rank, oversample))
+    return report(WL_ENOSPACE, "workspace too small", -1, hipSuccess);
+  const int l = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(rank) + oversample, std::min(N, K)));
+  Dev d;
+  d.s = static_cast<hipStream_t>(stream);
+  uint8_t *ws = static_cast<uint8_t *>(d_ws);
+  auto take = [&ws](size_t elems) {
+    float *p = reinterpret_cast<float *>(ws);
+    ws += align256(elems * 4);
+    return p;
+  };
+  float *R = take(static_cast<size_t>(N) * K);
+  float *Y = take(static_cast<size_t>(N) * l), *Y2 = take(static_cast<size_t>(N) * l);
+  float *Z = take(static_cast<size_t>(K) * l), *Z2 = take(static_cast<size_t>(K) * l);
+  float *B = take(static_cast<size_t>(l) * K);
+  float *small = take(static_cast<size_t>(l) * l);
+  float *F = take(static_cast<size_t>(std::max(N, K)) * rank);
+
+  const uint16_t *W = static_cast<const uint16_t *>(d_w);
+  uint16_t *W0 = static_cast<uint16_t *>(d_w0);
+  uint16_t *Uo = static_cast<uint16_t *>(d_u), *Vo = static_cast<uint16_t *>(d_v);
+  const size_t nk = static_cast<size_t>(N) * K;
+  d.err = wl::launch_band_mean(W, m, nk, W0, d.s);
+  if (!d.ok()) return report(WL_EHIP, "", -1, d.err);
+  for (int layer = 0; layer < m; ++layer) {
+    d.err = wl::launch_scale_residual(W + layer * nk, W0, N, K, d_s + static_cast<size_t>(layer) * N, R, d.s);
+    if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
+    if (rank == 0) continue;
+    uint16_t *u = Uo + static_cast<size_t>(layer) * N * rank, *v = Vo + static_cast<size_t>(layer) * K * rank;
+    // range finder: Y = R Omega, then q rounds of Z = R^T Y, Y = R Z
+    d.err = wl::launch_gemm_f32(R, K, 1, d_omega, l, 1, Y, l, N, l, K, d.s);
+    Orth o = d.ok() ? orthonormalize(d, Y, Y2, N, l, small) : kOrthFail;
+    for (int it = 0; it < power_iters && o == kOrthOk; ++it) {
+      d.err = wl::launch_gemm_f32(R, 1, K, Y, l, 1, Z, l, K, l, N, d.s);  // Z = R^T Y
+      o = d.ok() ? orthonormalize(d, Z, Z2, K, l, small) : kOrthFail;
+      if (o != kOrthOk) break;
+      d.err = wl::launch_gemm_f32(R, K, 1, Z, l, 1, Y, l, N, l, K, d.s);  // Y = R Z
+      o = d.ok() ? orthonormalize(d, Y, Y2, N, l, small) : kOrthFail;
+    }
+    if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
+    if (o == kOrthFail) return report(WL_EINVAL, "range basis is not numerically positive definite (non-finite weights?)", layer, hipSuccess);
+    if (o == kOrthZero) {  // R Omega = 0: the residual is zero, so is its delta
+      d.err = hipMemsetAsync(u, 0, static_cast<size_t>(N) * rank * 2, d.s);
+      if (d.ok()) d.err = hipMemsetAsync(v, 0, static_cast<size_t>(K) * rank * 2, d.s);
+      if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
+      continue;
+    }
+    // B = Q^T R [l, K]; B B^T = W Lambda W^T on the host
+    d.err = wl::launch_gemm_f32(Y, 1, l, R, K, 1, B, K, l, K, N, d.s);
+    if (d.ok()) d.err = wl::launch_gemm_f32(B, K, 1, B, 1, K, small, l, l, l, K, d.s);
+    std::vector<double> C = d.get(small, static_cast<size_t>(l) * l), lam, Wv;
+    if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
+    jacobi_eigen(C, l, lam, Wv);
+    std::vector<double> Su(static_cast<size_t>(l) * rank), Sv(static_cast<size_t>(l) * rank);
+    for (int c = 0; c < rank; ++c) {
+      const double sig = std::sqrt(std::max(lam[c], 0.0));
+      const double root = std::sqrt(sig);
+      for (int i = 0; i < l; ++i) {
+        Su[static_cast<size_t>(i) * rank + c] = Wv[static_cast<size_t>(i) * l + c] * root;
+        Sv[static_cast<size_t>(i) * rank + c] = sig > 0.0 ? Wv[static_cast<size_t>(i) * l + c] / root : 0.0;
+      }
+    }
+    // U = Q Su [N, r], V = B^T Sv [K, r], rounded to bf16
+    d.put(small, Su);
+    if (d.ok()) d.err = wl::launch_gemm_f32(Y, l, 1, small, rank, 1, F, rank, N, rank, l, d.s);
+    if (d.ok()) d.err = wl::launch_to_bf16(F, static_cast<size_t>(N) * rank, u, d.s);
+    if (d.ok()) d.err = hipStreamSynchronize(d.s);
+    d.put(small, Sv);
+    if (d.ok()) d.err = wl::launch_gemm_f32(B, 1, K, small, rank, 1, F, rank, K, rank, l, d.s);
+    if (d.ok()) d.err = wl::launch_to_bf16(F, static_cast<size_t>(K) * rank, v, d.s);
+    if (d.ok()) d.err = hipStreamSynchronize(d.s);
+    if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
+  }
+  d.err = hipStreamSynchronize(d.s);
+  if (!d.ok()) return report(WL_EHIP, "", m - 1, d.err);
+  wl::set_last_error("");
+  return WL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Kernels of the GPU decomposition (one band of one family): band mean, the
+// per-row least-squares scale, the residual, and an fp32 GEMM with arbitrary
+// strides used by the randomized truncated SVD of the residual.  The steps
+// are the analytic decomposition of the "Add a new model architecture" page
+// ("Decompose HF weights") with these readings: band mean, per-row scale
+// s_i = <W_i, W0_i> / <W0_i, W0_i>, rank-r truncated SVD of W - diag(s) W0
+// split as U = P sqrt(S), V = Q sqrt(S).
+#include "common.h"
+#include "internal.h"
+
+namespace wl {
+
+namespace {
+
+// fp64 -> fp32 (nearest even) -> bf16 (nearest even): the stored rounding of
+// a value computed in fp64.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) { return f32_to_bf16(static_cast<float>(v)); }
+
+// W0 = bf16(sum_l W_l / m), the sum taken in fp64 in layer order.
+__global__ void band_mean_kernel(const uint16_t *W, int m, size_t nk, uint16_t *W0) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= nk) return;
+  double acc = 0.0;
+  for (int l = 0; l < m; ++l) acc += static_cast<double>(bf16_to_f32(W[static_cast<size_t>(l) * nk + i]));
+  W0[i] = f64_to_bf16(acc / m);
+}
+
+// s_i = <W_i, W0_i> / <W0_i, W0_i> in fp64 (1 for a zero W0 row), stored fp32;
+// then R_i = W_i - s_i W0_i in fp32.  One workgroup per row.
+__global__ void scale_residual_kernel(const uint16_t *W, const uint16_t *W0, int K, float *s, float *R) {
+  const int row = blockIdx.x;
+  const uint16_t *w = W + static_cast<size_t>(row) * K;
+  const uint16_t *w0 = W0 + static_cast<size_t>(row) * K;
+  double num = 0.0, den = 0.0;
+  for (int j = threadIdx.x; j < K; j += blockDim.x) {
+    const double a = bf16_to_f32(w[j]), b = bf16_to_f32(w0[j]);
+    num += a * b;
+    den += b * b;
+  }
+  __shared__ double rn[256], rd[256];
+  rn[threadIdx.x] = num;
+  rd[threadIdx.x] = den;
+  __syncthreads();
+  for (int st = blockDim.x / 2; st > 0; st >>= 1) {
+    if (static_cast<int>(threadIdx.x) < st) {
+      rn[threadIdx.x] += rn[threadIdx.x + st];
+      rd[threadIdx.x] += rd[threadIdx.x + st];
+    }
+    __syncthreads();
+  }
+  const float sv = rd[0] == 0.0 ? 1.f : static_cast<float>(rn[0] / rd[0]);
+  if (threadIdx.x == 0) s[row] = sv;
+  float *r = R + static_cast<size_t>(row) * K;
+  for (int j = threadIdx.x; j < K; j += blockDim.x) r[j] = bf16_to_f32(w[j]) - sv * bf16_to_f32(w0[j]);
+}
+
+// C[M][N] = sum_k A(m, k) B(k, n), A(m, k) = A[m * sam + k * sak], B(k, n) =
+// B[k * sbk + n * sbn], C row-major with ldc; fp32, 64 x 64 tiles, 16 k per
+// LDS tile, 256 threads with 4 x 4 outputs each.
+__global__ void gemm_f32_kernel(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn,
+                                float *C, int64_t ldc, int M, int N, int K) {
+  __shared__ float As[16][65], Bs[16][65];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      const int kk = e & 15, mm = e >> 4;  // A tile: 64 rows x 16 k
+      const int gm = m0 + mm, gk = k0 + kk;
+      As[kk][mm] = (gm < M && gk < K) ? A[gm * sam + gk * sak] : 0.f;
+      const int nn = e & 63, kb = e >> 6;  // B tile: 16 k x 64 cols
+      const int gn = n0 + nn, gk2 = k0 + kb;
+      Bs[kb][nn] = (gn < N && gk2 < K) ? B[gk2 * sbk + gn * sbn] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gm = m0 + ty * 4 + i;
+    if (gm >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gn = n0 + tx * 4 + j;
+      if (gn < N) C[gm * ldc + gn] = acc[i][j];
+    }
+  }
+}
+
+// fp32 -> bf16 (nearest even), n elements.
+__global__ void to_bf16_kernel(const float *src, size_t n, uint16_t *dst) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = f32_to_bf16(src[i]);
+}
+
+unsigned blocks_for(size_t n) { return static_cast<unsigned>((n + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_band_mean(const uint16_t *W, int m, size_t nk, uint16_t *W0, hipStream_t stream) {
+  hipLaunchKernelGGL(band_mean_kernel, dim3(blocks_for(nk)), dim3(256), 0, stream, W, m, nk, W0);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_residual(const uint16_t *W, const uint16_t *W0, int N, int K, float *s, float *R,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(scale_residual_kernel, dim3(N), dim3(256), 0, stream, W, W0, K, s, R);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn, float *C,
+                           int64_t ldc, int M, int N, int K, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, stream, A, sam, sak, B, sbk,
+                     sbn, C, ldc, M, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float *src, size_t n, uint16_t *dst, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, src, n, dst);
+  return hipGetLastError();
+}
+
+}  // namespace wl

@@ -440,6 +440,10 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
 
 }  // namespace
 
+namespace wl {
+void set_last_error(const char *msg) { g_err = msg ? msg : ""; }
+}  // namespace wl
+
 extern "C" {
 
 const char *wl_last_error(void) { return g_err.c_str(); }
