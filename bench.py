@@ -14,7 +14,9 @@ The same run also times
     T=2048, 7 single-family calls per layer), in TFLOP/s,
   * per-launch kernel durations with HIP events on the launch stream (the
     roofline figure), and
-  * the fp64 CPU oracle on a bounded sample of the headline workload.
+  * the fp64 CPU oracle on a bounded sample of the headline workload,
+  * the GPU decomposition of the Gemma-3-1B-shaped model (13 bands x 7
+    families, rank 32) against the oracle's exact decomposition.
 
 Prints one JSON line.  Runs on one GPU only.
 """
@@ -388,6 +390,71 @@ def cpu_baseline(wl, T, budget_s, dev):
                       f"of bundle bytes), repeated {n}x in {el:.1f} s; W0/s/U/V pre-upcast to fp64 outside the timing"}
 
 
+def decompose_flops(m, n, k, rank, over, q):
+    """Algorithmic fp32 flops of the GPU decomposition of one band: per layer
+    the products with the residual (R Omega, q rounds of R^T Y and R Z,
+    B = Q^T R: 2 N K l each), the Cholesky-QR passes (Gram and Y T, 2 n l^2
+    each; one pass between products, three on the final basis), B B^T and
+    the two factor products."""
+    l = min(rank + over, n, k)
+    if rank == 0:
+        return 0
+    per = 2 * n * k * l * (1 + 2 * q + 1)
+    passes_y = (1 + (q - 1) + 3) if q > 0 else 3          # row-space bases (n = N)
+    passes_z = q                                           # column-space bases (n = K)
+    per += passes_y * 4 * n * l * l + passes_z * 4 * k * l * l
+    per += 2 * l * l * k + 2 * n * l * rank + 2 * k * l * rank
+    return m * per
+
+
+def decompose_section(dev, rank=32, over=16, q=4, cpu_budget=0.0):
+    """GPU decomposition of the Gemma-3-1B-shaped model: 26 layers in 13
+    bands (two layers per band), 7 families, rank 32: 91 band decompositions
+    (182 matrices) from seeded i.i.d. N(0, 1/in) bf16 layer weights already
+    resident in HBM."""
+    import torch
+    import synth
+    from weight_shared_rank_amd import binding
+    wl = synth.workload(2)
+    shapes = [wl.shape(0, f) for f in synth.FAMILIES]
+    inputs = []
+    for b in range(13):
+        for fi, (n, k) in enumerate(shapes):
+            w = synth.band_layers(1000 + 16 * b + fi, 2, n, k, device=dev)
+            om = synth.sketch_matrix(7 + fi, k, binding.sketch_columns(n, k, rank, over), dev)
+            inputs.append((w, om))
+    flops = sum(decompose_flops(2, w.shape[1], w.shape[2], rank, over, q) for w, _ in inputs)
+    torch.cuda.synchronize()
+    for w, om in inputs[:7]:  # warm-up: one band of every family
+        binding.decompose(w, rank, om, oversample=over, power_iters=q)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for w, om in inputs:
+        binding.decompose(w, rank, om, oversample=over, power_iters=q)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    out = {"workload": "gemma3-1b decomposition: 13 bands x 7 families (q, k, v, o, gate, up, down), two layers "
+                       "per band, rank 32, oversample 16, 4 power rounds",
+           "matrices": 2 * len(inputs), "seconds": el, "matrices_per_s": 2 * len(inputs) / el,
+           "fp32_flops": flops, "fp32_TFLOPs": flops / el / 1e12}
+    if cpu_budget > 0:
+        import numpy as np
+        from oracle import decompose
+        # the oracle's exact decomposition (numpy SVD) of bands of the gate family until the budget is spent
+        w = inputs[4][0].float().cpu().double().numpy()
+        n = 0
+        t1 = time.perf_counter()
+        while True:
+            decompose.decompose_band([w[0], w[1]], rank, store=True)
+            n += 2
+            if time.perf_counter() - t1 >= cpu_budget:
+                break
+        cel = time.perf_counter() - t1
+        out["cpu_oracle"] = {"matrices_per_s": n / cel, "sample": f"{n} gate matrices (4096 x 1152) decomposed by "
+                             f"the fp64 oracle (full SVD) in {cel:.1f} s"}
+    return out
+
+
 def band_reuse(dev, reps=5):
     """Band reuse of W0 (decode, T=1).  For two consecutive layers l, l+1 of
     one band, the second call reads the same W0 bytes as the first.  Three
@@ -486,7 +553,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill", "dense", "act", "fp8"])
+    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill", "dense", "act", "fp8",
+                                                             "decompose"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--band-reuse", action="store_true",
                     help="report whether a band-shared W0 re-read by the next layer is served from the 256 MB "
@@ -562,6 +630,11 @@ def main():
         singles = tuple((f, (f,)) for f in synth.FAMILIES)
         res["prefill3"] = prefill_section(synth.workload(3), 2048, singles, args.steps, args.warmup, dev)
         log(f"prefill w3: {res['prefill3']['TFLOPs']:.1f} TFLOP/s")
+
+    if args.only in ("all", "decompose"):
+        res["decompose_gemma3"] = decompose_section(dev, cpu_budget=0.0 if args.no_cpu else 4.0)
+        log(f"decomposition: {res['decompose_gemma3']['matrices_per_s']:.1f} matrices/s, "
+            f"{res['decompose_gemma3']['seconds']:.2f} s for the gemma3 model")
 
     line = {"metric": "weightless-linear decode GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

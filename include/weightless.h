@@ -216,10 +216,12 @@ wl_status weightless_materialize(const wl_bundle *bundle, int32_t layer, int32_t
  *   U = P sqrt(S), V = Q sqrt(S), stored bf16.
  * The SVD is randomized subspace iteration (Halko, Martinsson and Tropp,
  * 2011): l = min(rank + oversample, N, K) sketch columns, power_iters rounds,
- * fp32 GPU products, Cholesky-QR twice for each orthonormalization and a
- * Jacobi eigen-solve of the l x l Gram matrix on the host.  Its delta is the
- * exact truncated SVD's up to the sketch's accuracy: the error approaches
- * Eckart-Young's as power_iters grows and is exact when rank(R) <= l.
+ * fp32 GPU products, Cholesky-QR orthonormalization (one pass between
+ * products, three for the final basis; the l x l factorizations on the host
+ * in fp64) and a Jacobi eigen-solve of the l x l matrix B B^T on the host.
+ * Its delta is the exact truncated SVD's up to the sketch's accuracy: the
+ * error approaches Eckart-Young's as power_iters grows and is exact when
+ * rank(R) <= l (oversample 16 and 4 rounds stay within 1% on flat spectra).
  *
  * Workspace bytes for one call (fp32 residual, sketches and factors); 0 if
  * an argument is out of range. */

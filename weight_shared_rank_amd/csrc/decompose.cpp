@@ -115,12 +115,25 @@ void jacobi_eigen(std::vector<double> a, int n, std::vector<double> &lam, std::v
 struct Dev {
   hipStream_t s;
   hipError_t err = hipSuccess;
+  float *part = nullptr;  // split-K partials of the fp32 GEMMs
+  size_t part_elems = 0;
+  std::vector<float> up_u, up_v;  // host sources of in-flight uploads (alive until the next sync)
   bool ok() const { return err == hipSuccess; }
+  hipError_t gemm(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn, float *C,
+                  int64_t ldc, int M, int N, int K) {
+    return wl::launch_gemm_f32(A, sam, sak, B, sbk, sbn, C, ldc, M, N, K, part, part_elems, s);
+  }
   void put(float *d, const std::vector<double> &h) {
     if (!ok()) return;
     std::vector<float> f(h.begin(), h.end());
     err = hipMemcpyAsync(d, f.data(), f.size() * 4, hipMemcpyHostToDevice, s);
     if (ok()) err = hipStreamSynchronize(s);
+  }
+  // Asynchronous upload from a host vector that stays alive until the next sync.
+  void put_async(float *d, std::vector<float> &keep, const std::vector<double> &h) {
+    if (!ok()) return;
+    keep.assign(h.begin(), h.end());
+    err = hipMemcpyAsync(d, keep.data(), keep.size() * 4, hipMemcpyHostToDevice, s);
   }
   std::vector<double> get(const float *d, size_t n) {
     std::vector<float> f(n);
@@ -130,13 +143,16 @@ struct Dev {
   }
 };
 
-// Y [n x l] <- Y T with Y^T Y = L L^T and T = L^-T, done twice (CholQR2).
-// A rank-deficient Y gets a small diagonal shift before the first factoring
-// (shifted Cholesky-QR); tmp is another n x l buffer.
+// Y [n x l] <- Y T with Y^T Y = L L^T and T = L^-T, repeated `passes` times
+// (Cholesky-QR).  The l x l Gram matrix is formed on the device and factored
+// on the host in fp64 (for the l of a sketch, one host round trip measured
+// faster than a one-wavefront device factorization).  A rank-deficient Y
+// gets a small diagonal shift (shifted Cholesky-QR); the following pass
+// restores orthonormality.  tmp is another n x l buffer.
 enum Orth { kOrthOk, kOrthZero, kOrthFail };
-Orth orthonormalize(Dev &d, float *&Y, float *&tmp, int n, int l, float *small) {
-  for (int pass = 0; pass < 2 && d.ok(); ++pass) {
-    d.err = wl::launch_gemm_f32(Y, 1, l, Y, l, 1, small, l, l, l, n, d.s);  // G = Y^T Y
+Orth orthonormalize(Dev &d, float *&Y, float *&tmp, int n, int l, float *small, int passes) {
+  for (int pass = 0; pass < passes && d.ok(); ++pass) {
+    d.err = d.gemm(Y, 1, l, Y, l, 1, small, l, l, l, n);  // G = Y^T Y
     std::vector<double> G = d.get(small, static_cast<size_t>(l) * l);
     if (!d.ok()) return kOrthFail;
     double tr = 0.0;
@@ -145,19 +161,22 @@ Orth orthonormalize(Dev &d, float *&Y, float *&tmp, int n, int l, float *small) 
     if (!std::isfinite(tr)) return kOrthFail;
     std::vector<double> L = G;
     bool good = cholesky(L, l);
-    for (int attempt = 0; !good && attempt < 6; ++attempt) {
+    for (int attempt = 1; !good && attempt < 8; ++attempt) {
       L = G;
-      const double shift = tr / l * std::pow(10.0, -7 + attempt);
+      const double shift = tr / l * std::pow(10.0, -8 + attempt);
       for (int i = 0; i < l; ++i) L[i * l + i] += shift;
       good = cholesky(L, l);
     }
     if (!good) return kOrthFail;
     d.put(small, inv_lower_transpose(L, l));
-    if (d.ok()) d.err = wl::launch_gemm_f32(Y, l, 1, small, l, 1, tmp, l, n, l, l, d.s);  // Y T
+    if (d.ok()) d.err = d.gemm(Y, l, 1, small, l, 1, tmp, l, n, l, l);  // Y T
     std::swap(Y, tmp);
   }
   return d.ok() ? kOrthOk : kOrthFail;
 }
+
+// Split-K partials: up to 16 slices of the largest product output (max(N, K) x l).
+size_t part_elems(int N, int K, size_t l) { return 16 * static_cast<size_t>(std::max(N, K)) * l; }
 
 wl_status report(wl_status st, const char *what, int layer, hipError_t e) {
   char buf[256];
@@ -181,7 +200,9 @@ size_t weightless_decompose_workspace_bytes(int32_t N, int32_t K, int32_t rank, 
   n += 2 * align256(static_cast<size_t>(K) * l * 4);          // Z, spare
   n += align256(l * K * 4);                                   // B
   n += align256(l * l * 4);                                   // small
-  n += align256(static_cast<size_t>(std::max(N, K)) * rank * 4);  // U or V in fp32
+  n += align256(static_cast<size_t>(N) * rank * 4);                // U in fp32
+  n += align256(static_cast<size_t>(K) * rank * 4);                // V in fp32
+  n += align256(part_elems(N, K, l) * 4);                          // split-K partials
   return n;
 }
 
@@ -210,7 +231,9 @@ wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K,
   float *Z = take(static_cast<size_t>(K) * l), *Z2 = take(static_cast<size_t>(K) * l);
   float *B = take(static_cast<size_t>(l) * K);
   float *small = take(static_cast<size_t>(l) * l);
-  float *F = take(static_cast<size_t>(std::max(N, K)) * rank);
+  float *F = take(static_cast<size_t>(N) * rank), *F2 = take(static_cast<size_t>(K) * rank);
+  d.part_elems = part_elems(N, K, l);
+  d.part = take(d.part_elems);
 
   const uint16_t *W = static_cast<const uint16_t *>(d_w);
   uint16_t *W0 = static_cast<uint16_t *>(d_w0);
@@ -223,15 +246,18 @@ wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K,
     if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
     if (rank == 0) continue;
     uint16_t *u = Uo + static_cast<size_t>(layer) * N * rank, *v = Vo + static_cast<size_t>(layer) * K * rank;
-    // range finder: Y = R Omega, then q rounds of Z = R^T Y, Y = R Z
-    d.err = wl::launch_gemm_f32(R, K, 1, d_omega, l, 1, Y, l, N, l, K, d.s);
-    Orth o = d.ok() ? orthonormalize(d, Y, Y2, N, l, small) : kOrthFail;
+    // range finder: Y = R Omega, then q rounds of Z = R^T Y, Y = R Z.  The
+    // bases between products only need to stay well conditioned (one
+    // Cholesky-QR pass); the final one, which B = Q^T R and U = Q W use,
+    // gets three (shifted Cholesky-QR3 when the first pass needs a shift).
+    d.err = d.gemm(R, K, 1, d_omega, l, 1, Y, l, N, l, K);
+    Orth o = d.ok() ? orthonormalize(d, Y, Y2, N, l, small, power_iters == 0 ? 3 : 1) : kOrthFail;
     for (int it = 0; it < power_iters && o == kOrthOk; ++it) {
-      d.err = wl::launch_gemm_f32(R, 1, K, Y, l, 1, Z, l, K, l, N, d.s);  // Z = R^T Y
-      o = d.ok() ? orthonormalize(d, Z, Z2, K, l, small) : kOrthFail;
+      d.err = d.gemm(R, 1, K, Y, l, 1, Z, l, K, l, N);  // Z = R^T Y
+      o = d.ok() ? orthonormalize(d, Z, Z2, K, l, small, 1) : kOrthFail;
       if (o != kOrthOk) break;
-      d.err = wl::launch_gemm_f32(R, K, 1, Z, l, 1, Y, l, N, l, K, d.s);  // Y = R Z
-      o = d.ok() ? orthonormalize(d, Y, Y2, N, l, small) : kOrthFail;
+      d.err = d.gemm(R, K, 1, Z, l, 1, Y, l, N, l, K);  // Y = R Z
+      o = d.ok() ? orthonormalize(d, Y, Y2, N, l, small, it + 1 == power_iters ? 3 : 1) : kOrthFail;
     }
     if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
     if (o == kOrthFail) return report(WL_EINVAL, "range basis is not numerically positive definite (non-finite weights?)", layer, hipSuccess);
@@ -242,8 +268,8 @@ wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K,
       continue;
     }
     // B = Q^T R [l, K]; B B^T = W Lambda W^T on the host
-    d.err = wl::launch_gemm_f32(Y, 1, l, R, K, 1, B, K, l, K, N, d.s);
-    if (d.ok()) d.err = wl::launch_gemm_f32(B, K, 1, B, 1, K, small, l, l, l, K, d.s);
+    d.err = d.gemm(Y, 1, l, R, K, 1, B, K, l, K, N);
+    if (d.ok()) d.err = d.gemm(B, K, 1, B, 1, K, small, l, l, l, K);
     std::vector<double> C = d.get(small, static_cast<size_t>(l) * l), lam, Wv;
     if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
     jacobi_eigen(C, l, lam, Wv);
@@ -256,15 +282,14 @@ wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K,
         Sv[static_cast<size_t>(i) * rank + c] = sig > 0.0 ? Wv[static_cast<size_t>(i) * l + c] / root : 0.0;
       }
     }
-    // U = Q Su [N, r], V = B^T Sv [K, r], rounded to bf16
-    d.put(small, Su);
-    if (d.ok()) d.err = wl::launch_gemm_f32(Y, l, 1, small, rank, 1, F, rank, N, rank, l, d.s);
+    // U = Q Su [N, r], V = B^T Sv [K, r], rounded to bf16 (no sync: the next
+    // layer's round trip, or the final sync, completes them)
+    d.put_async(small, d.up_u, Su);
+    if (d.ok()) d.err = d.gemm(Y, l, 1, small, rank, 1, F, rank, N, rank, l);
     if (d.ok()) d.err = wl::launch_to_bf16(F, static_cast<size_t>(N) * rank, u, d.s);
-    if (d.ok()) d.err = hipStreamSynchronize(d.s);
-    d.put(small, Sv);
-    if (d.ok()) d.err = wl::launch_gemm_f32(B, 1, K, small, rank, 1, F, rank, K, rank, l, d.s);
-    if (d.ok()) d.err = wl::launch_to_bf16(F, static_cast<size_t>(K) * rank, v, d.s);
-    if (d.ok()) d.err = hipStreamSynchronize(d.s);
+    d.put_async(Z2, d.up_v, Sv);
+    if (d.ok()) d.err = d.gemm(B, 1, K, Z2, rank, 1, F2, rank, K, rank, l);
+    if (d.ok()) d.err = wl::launch_to_bf16(F2, static_cast<size_t>(K) * rank, v, d.s);
     if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
   }
   d.err = hipStreamSynchronize(d.s);

@@ -5,6 +5,8 @@
 // ("Decompose HF weights") with these readings: band mean, per-row scale
 // s_i = <W_i, W0_i> / <W0_i, W0_i>, rank-r truncated SVD of W - diag(s) W0
 // split as U = P sqrt(S), V = Q sqrt(S).
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -55,22 +57,27 @@ __global__ void scale_residual_kernel(const uint16_t *W, const uint16_t *W0, int
 }
 
 // C[M][N] = sum_k A(m, k) B(k, n), A(m, k) = A[m * sam + k * sak], B(k, n) =
-// B[k * sbk + n * sbn], C row-major with ldc; fp32, 64 x 64 tiles, 16 k per
-// LDS tile, 256 threads with 4 x 4 outputs each.
+// B[k * sbk + n * sbn]; fp32, 64 x 64 tiles, 16 k per LDS tile, 256 threads
+// with 4 x 4 outputs each.  blockIdx.z takes the k range [z kc, (z+1) kc);
+// with gridDim.z > 1 each slice writes its own partial C_z at C + z M ldc and
+// reduce_kernel adds them in slice order (deterministic).  Tile loads walk
+// the operand's unit-stride index fastest (a_m_fast: sam == 1).
 __global__ void gemm_f32_kernel(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn,
-                                float *C, int64_t ldc, int M, int N, int K) {
+                                float *C, int64_t ldc, int M, int N, int K, int kc, int a_m_fast, int b_n_fast) {
   __shared__ float As[16][65], Bs[16][65];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int kbeg = blockIdx.z * kc, kend = min(K, kbeg + kc);
+  C += static_cast<int64_t>(blockIdx.z) * M * ldc;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
     for (int e = threadIdx.x; e < 16 * 64; e += 256) {
-      const int kk = e & 15, mm = e >> 4;  // A tile: 64 rows x 16 k
+      const int kk = a_m_fast ? (e >> 6) : (e & 15), mm = a_m_fast ? (e & 63) : (e >> 4);
       const int gm = m0 + mm, gk = k0 + kk;
-      As[kk][mm] = (gm < M && gk < K) ? A[gm * sam + gk * sak] : 0.f;
-      const int nn = e & 63, kb = e >> 6;  // B tile: 16 k x 64 cols
+      As[kk][mm] = (gm < M && gk < kend) ? A[gm * sam + gk * sak] : 0.f;
+      const int kb = b_n_fast ? (e >> 6) : (e & 15), nn = b_n_fast ? (e & 63) : (e >> 4);
       const int gn = n0 + nn, gk2 = k0 + kb;
-      Bs[kb][nn] = (gn < N && gk2 < K) ? B[gk2 * sbk + gn * sbn] : 0.f;
+      Bs[kb][nn] = (gn < N && gk2 < kend) ? B[gk2 * sbk + gn * sbn] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -99,6 +106,17 @@ __global__ void gemm_f32_kernel(const float *A, int64_t sam, int64_t sak, const 
   }
 }
 
+// C[m][n] = sum over z = 0 .. splits-1, in order, of P[z][m][n] (P dense
+// [splits][M][N]).
+__global__ void reduce_kernel(const float *P, int splits, int M, int N, float *C, int64_t ldc) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t mn = static_cast<int64_t>(M) * N;
+  if (i >= mn) return;
+  float acc = 0.f;
+  for (int z = 0; z < splits; ++z) acc += P[z * mn + i];
+  C[(i / N) * ldc + i % N] = acc;
+}
+
 // fp32 -> bf16 (nearest even), n elements.
 __global__ void to_bf16_kernel(const float *src, size_t n, uint16_t *dst) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -120,11 +138,44 @@ hipError_t launch_scale_residual(const uint16_t *W, const uint16_t *W0, int N, i
   return hipGetLastError();
 }
 
+int gemm_f32_splits(int M, int N, int K, size_t part_elems) {
+  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  const int want = (512 + tiles - 1) / tiles;
+  int splits = std::min(want, std::max(1, (K + 63) / 64));
+  const size_t mn = static_cast<size_t>(M) * N;
+  if (mn == 0 || splits < 2 || part_elems < 2 * mn) return 1;
+  splits = static_cast<int>(std::min<size_t>(splits, part_elems / mn));
+  return std::max(splits, 1);
+}
+
+namespace {
+int split_chunk(int K, int &splits) {
+  int kc = std::max(K, 1);
+  if (splits > 1) {
+    kc = ((K + splits - 1) / splits + 15) / 16 * 16;
+    splits = (K + kc - 1) / kc;
+  }
+  return kc;
+}
+}  // namespace
+
 hipError_t launch_gemm_f32(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn, float *C,
-                           int64_t ldc, int M, int N, int K, hipStream_t stream) {
+                           int64_t ldc, int M, int N, int K, float *part, size_t part_elems, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, stream, A, sam, sak, B, sbk,
-                     sbn, C, ldc, M, N, K);
+  int splits = part ? gemm_f32_splits(M, N, K, part_elems) : 1;
+  const int kc = split_chunk(K, splits);
+  const dim3 grid((N + 63) / 64, (M + 63) / 64, splits);
+  if (splits == 1) {
+    hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, stream, A, sam, sak, B, sbk, sbn, C, ldc, M, N, K, kc,
+                       sam == 1 ? 1 : 0, sbn == 1 ? 1 : 0);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, stream, A, sam, sak, B, sbk, sbn, part,
+                     static_cast<int64_t>(N), M, N, K, kc, sam == 1 ? 1 : 0, sbn == 1 ? 1 : 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t mn = static_cast<size_t>(M) * N;
+  hipLaunchKernelGGL(reduce_kernel, dim3(blocks_for(mn)), dim3(256), 0, stream, part, splits, M, N, C, ldc);
   return hipGetLastError();
 }
 

@@ -83,12 +83,14 @@ hipError_t launch_dequantize_rows(const uint8_t *src, int32_t Kp, const float *q
 // Decomposition (one band of one family): W0 = bf16(mean of the m layers
 // W [m][nk]); per layer s [N] (LS row scale, fp32) and R = W - s W0 (fp32
 // [N][K]); a strided fp32 GEMM C = A B with A(m,k) = A[m*sam + k*sak] and
-// B(k,n) = B[k*sbk + n*sbn]; fp32 -> bf16.
+// B(k,n) = B[k*sbk + n*sbn], splitting K over up to part_elems / (M N)
+// slices whose fp32 partials go to part (NULL: no split); fp32 -> bf16.
 hipError_t launch_band_mean(const uint16_t *W, int m, size_t nk, uint16_t *W0, hipStream_t stream);
 hipError_t launch_scale_residual(const uint16_t *W, const uint16_t *W0, int N, int K, float *s, float *R,
                                  hipStream_t stream);
 hipError_t launch_gemm_f32(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn,
-                           float *C, int64_t ldc, int M, int N, int K, hipStream_t stream);
+                           float *C, int64_t ldc, int M, int N, int K, float *part, size_t part_elems,
+                           hipStream_t stream);
 hipError_t launch_to_bf16(const float *src, size_t n, uint16_t *dst, hipStream_t stream);
 
 // Text of wl_last_error() for failures reported outside weightless.cpp.
