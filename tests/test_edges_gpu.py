@@ -216,3 +216,34 @@ def test_split_k_prefill(gpu_lib, T):
             ref_call = "k" if (c == "v" and wl.layer_types[layer] == 1) else c   # tied: v is k's output
             res = compare(np64(y), ow.call(layer, ref_call, np64(x)))
             assert res["ok"], f"layer {layer} {c}: {res}"
+
+
+@pytest.mark.parametrize("T", [1, 16, 40, 130])
+def test_outputs_with_two_byte_alignment(gpu_lib, T):
+    """y (and the fused gate|up h) need only 2-byte alignment: outputs written
+    at an odd element offset are bitwise the aligned outputs (vector stores are
+    taken only where the destination allows them)."""
+    wl = ragged(5, layer_types=(0, 1), k_eq_v=(1,), bands=1)
+    b = sdev.load(wl, DEV)
+    for layer in range(2):
+        for c in ("qkv", "gate_up", "o", "down"):
+            x = wl.x(layer, c, T, DEV)
+            announce(f"2-byte aligned y T={T} layer {layer} {c}")
+            y = call(b, layer, c, x)
+            n = y.shape[1]
+            buf = torch.zeros(T * n + 1, dtype=torch.bfloat16, device=DEV)
+            yo = buf[1:].view(T, n)
+            if c in ("qkv", "gate_up"):
+                b.stacked(layer, c, x, y=yo)
+            else:
+                b.linear(layer, c, x, y=yo)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), yo.view(torch.int16)), f"layer {layer} {c}"
+        x = wl.x(layer, "gate_up", T, DEV)
+        h = b.gate_up_act(layer, "gelu_tanh", x)
+        n = h.shape[1]
+        buf = torch.zeros(T * n + 1, dtype=torch.bfloat16, device=DEV)
+        ho = buf[1:].view(T, n)
+        b.gate_up_act(layer, "gelu_tanh", x, h=ho)
+        torch.cuda.synchronize()
+        assert torch.equal(h.view(torch.int16), ho.view(torch.int16)), f"layer {layer} gate_up_act"

@@ -7,8 +7,8 @@
 // The truncated SVD of each residual R [N, K] is randomized subspace
 // iteration (Halko, Martinsson and Tropp, "Finding structure with
 // randomness", 2011): Y = R Omega with l = r + p columns, q rounds of
-// Z = R^T Y, Y = R Z, each product orthonormalized by Cholesky-QR done twice;
-// then B = Q^T R, the small symmetric eigenproblem B B^T = W Lambda W^T on
+// Z = R^T Y, Y = R Z, each product orthonormalized by Cholesky-QR (one pass
+// between products, three on the final basis); then B = Q^T R, the small symmetric eigenproblem B B^T = W Lambda W^T on
 // the host in double (cyclic Jacobi), sigma = sqrt(Lambda), U = Q W_r
 // sqrt(sigma_r), V = B^T W_r / sqrt(sigma_r).  The products run on the GPU in
 // fp32; the host sees only l x l matrices.  The test matrix Omega is the

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
         uint16_t o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(activation(a.act, acc[i][j][e]) * u[e]);
-        if (nv == 4 && ((a.ldh | jj) & 3) == 0) {
+        if (nv == 4 && (reinterpret_cast<uintptr_t>(hrow + jj) & 7) == 0) {
           *reinterpret_cast<uint2 *>(hrow + jj) =
               make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
         } else {
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
           if (e < nv) o[e] = f32_to_bf16(acc[i][j][e] + sc * bf16_to_f32(wrow[row + e]));
       }
       if (a.mode == kStoreBf16 || a.mode == kAddScaled) {
-        if (nv == 4 && ((a.ldy | row) & 3) == 0) {
+        if (nv == 4 && (reinterpret_cast<uintptr_t>(yrow + row) & 7) == 0) {
           *reinterpret_cast<uint2 *>(yrow + row) =
               make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
         } else {
@@ -396,16 +396,29 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
             if (e < nv) yrow[row + e] = o[e];
         }
       } else {
+        int ci = 0;
+        while (ci + 1 < a.nchild && row >= a.ch[ci + 1].row_start) ++ci;
+        const ChildDesc &ch = a.ch[ci];
+        const int jj = row - ch.row_start;
+        uint16_t *p0 = yrow + ch.y_off + jj, *p1 = ch.dup_off >= 0 ? yrow + ch.dup_off + jj : p0;
+        if (nv == 4 && jj + 4 <= ch.N && ((reinterpret_cast<uintptr_t>(p0) | reinterpret_cast<uintptr_t>(p1)) & 7) == 0) {
+          // the four rows are one child's: one 8-byte store (and its K=V copy)
+          const uint2 pk = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
+                                      o[2] | (static_cast<uint32_t>(o[3]) << 16));
+          *reinterpret_cast<uint2 *>(p0) = pk;
+          if (ch.dup_off >= 0) *reinterpret_cast<uint2 *>(p1) = pk;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (e >= nv) break;
-          const int r = row + e;
-          int ci = 0;
-          while (ci + 1 < a.nchild && r >= a.ch[ci + 1].row_start) ++ci;
-          const ChildDesc &ch = a.ch[ci];
-          const int jj = r - ch.row_start;
-          yrow[ch.y_off + jj] = o[e];
-          if (ch.dup_off >= 0) yrow[ch.dup_off + jj] = o[e];
+          for (int e = 0; e < 4; ++e) {
+            if (e >= nv) break;
+            const int r = row + e;
+            int cj = ci;
+            while (cj + 1 < a.nchild && r >= a.ch[cj + 1].row_start) ++cj;
+            const ChildDesc &c2 = a.ch[cj];
+            const int j2 = r - c2.row_start;
+            yrow[c2.y_off + j2] = o[e];
+            if (c2.dup_off >= 0) yrow[c2.dup_off + j2] = o[e];
+          }
         }
       }
     }
