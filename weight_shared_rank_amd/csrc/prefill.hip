@@ -140,15 +140,32 @@ __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16]
     const int gq = wave * TL::LPW + q;
     ldsoff[q] = gq < TL::GA ? gq * 1024 : BM * kRowBytes + (gq - TL::GA) * 1024;
   }
-  auto issue = [&](int stage, int step) {
+  // Running source pointers, one per load instruction, advanced by one stage
+  // per issue (stages are issued in order); a lane without a row reads the
+  // zero row and never advances.  Only a last step that reaches past klen
+  // (K not a multiple of 64) needs the per-chunk bound.
+  const uint16_t *cur[TL::LPW];
+  int inc[TL::LPW];
+#pragma unroll
+  for (int q = 0; q < TL::LPW; ++q) {
+    inc[q] = rp[q] != nullptr ? kBK : 0;
+    cur[q] = rp[q] != nullptr ? rp[q] + s_begin * kBK : zero_row;
+  }
+  const int full_steps = klen / kBK;
+  // loads q0 .. q1-1 of a stage
+  auto issue_part = [&](int stage, int step, int q0, int q1) {
+    const bool tail = step >= full_steps;
     const int k = step * kBK + lchunk * 8;
 #pragma unroll
     for (int q = 0; q < TL::LPW; ++q) {
-      const uint16_t *src = (rp[q] != nullptr && k < klen) ? rp[q] + step * kBK : zero_row;
+      if (q < q0 || q >= q1) continue;
+      const uint16_t *src = (tail && k >= klen) ? zero_row : cur[q];
       __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
                                        (lds_void *)(lds + stage * TL::STAGE + ldsoff[q]), 16, 0, 0);
+      cur[q] += inc[q];
     }
   };
+  auto issue = [&](int stage, int step) { issue_part(stage, step, 0, TL::LPW); };
   const int arow = (wm * TL::TM + r16) * kRowBytes;
   const int brow = BM * kRowBytes + (wn * TL::TN + r16) * kRowBytes;
   const int sw0 = ((0 + g) ^ (r16 & 7)) * 16, sw1 = ((4 + g) ^ (r16 & 7)) * 16;
@@ -165,20 +182,33 @@ __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16]
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (kt + NST - 1 < nk) issue((kt + NST - 1) % NST, s_begin + kt + NST - 1);
+    // the next stage's loads go out in two halves, before and between the
+    // two 32-k halves of this stage's MFMAs, so they interleave with the
+    // matrix work rather than queue up at once
+    const bool more = kt + NST - 1 < nk;
+    const int nstage = (kt + NST - 1) % NST, nstep = s_begin + kt + NST - 1;
+    if (more) issue_part(nstage, nstep, 0, TL::LPW / 2);
     const uint8_t *sb = lds + (kt % NST) * TL::STAGE;
+    // both halves' fragments are read up front (registers allow it: at most
+    // two waves per SIMD), so the LDS latency is paid once per stage
+    u32x4 fa[2][TL::FM], fb[2][TL::FN];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int sw = h ? sw1 : sw0;
-      u32x4 fa[TL::FM], fb[TL::FN];
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i) fa[i] = *reinterpret_cast<const u32x4 *>(sb + arow + i * 16 * kRowBytes + sw);
+      for (int i = 0; i < TL::FM; ++i)
+        fa[h][i] = *reinterpret_cast<const u32x4 *>(sb + arow + i * 16 * kRowBytes + sw);
 #pragma unroll
-      for (int j = 0; j < TL::FN; ++j) fb[j] = *reinterpret_cast<const u32x4 *>(sb + brow + j * 16 * kRowBytes + sw);
+      for (int j = 0; j < TL::FN; ++j)
+        fb[h][j] = *reinterpret_cast<const u32x4 *>(sb + brow + j * 16 * kRowBytes + sw);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[h][i], fb[h][j], acc[i][j]);
+      if (h == 0 && more) issue_part(nstage, nstep, TL::LPW / 2, TL::LPW);
     }
   }
   // every wave is done with the ring before it is refilled
@@ -198,8 +228,10 @@ __device__ __forceinline__ void unit_of(int id, int total, int nT, int nslices, 
   t = r % nT;
 }
 
+// At most two waves per SIMD (the LDS ring allows one workgroup per CU for
+// the big tiles), so the compiler may use up to 256 VGPRs per lane.
 template <int BM, int BN, int WM, int WN, int NST>
-__global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmArgs a) {
   using TL = Tile<BM, BN, WM, WN, NST>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
