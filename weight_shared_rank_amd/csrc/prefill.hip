@@ -34,10 +34,11 @@
 // with few rows (o, down, and Z = X V) split K into KS slices instead, so
 // that every CU streams.  Slices write fp32 partial tiles to the workspace;
 // a later launch sums them in slice order (deterministic): a reduce kernel
-// for Z, and for the main GEMM an elementwise finish kernel.  A split main
-// GEMM gets one more slice per tile, which computes the delta Z U^T on its
-// own (it is another K range of the same product, with U and Z as the
-// operands); the finish kernel forms s (.) sum(main slices) + delta.
+// for Z, and for the main GEMM an elementwise finish kernel.  On a split main
+// GEMM the last slice of each tile also computes the delta Z U^T (another K
+// range of the same product, with U and Z as the operands) into a partial of
+// its own, and takes that many fewer K steps, so the slices are balanced;
+// the finish kernel forms s (.) sum(K partials) + delta.
 // Partials are combined across launches, never across workgroups of one
 // launch: that would need device-scope release/acquire, which writes back /
 // invalidates a whole L2 on this part.
@@ -72,7 +73,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 enum Mode : int32_t {
   kStoreBf16 = 0,  // Y = bf16(acc), [T][ldy]
   kFused = 1,      // Y = child map of bf16(s (.) acc + Z U^T)
-  kPartial = 2,    // P[slice][T][M] = acc (fp32); slice ksplit (if nchild) = Z U^T
+  kPartial = 2,    // P[slice][T][M] = acc (fp32); the last slice also writes P[ksplit] = Z U^T (if nchild)
   kAddScaled = 3,  // Y = bf16(acc + s[t] * W[t][m]), [T][ldy] (effective-weight materialization)
   kFusedAct = 4,   // paired gate|up rows: H = bf16(act(s (.) gate + dg) * (s (.) up + du)), [T][ldh]
 };
@@ -228,6 +229,38 @@ __device__ __forceinline__ void unit_of(int id, int total, int nT, int nslices, 
   t = r % nT;
 }
 
+// fp32 partial of a tile (rows of the operand only) at P [T][M]: lane holds
+// tile rows v = wm*TM + 16i + 4g + e, token n0 + wn*TN + 16j + r16, mapped to
+// operand rows as in the kernel (plain or gate|up paired).
+template <int BM, int BN, int WM, int WN, int NST>
+__device__ __forceinline__ void store_partial_tile(const f32x4 (&acc)[BM / WM / 16][BN / WN / 16], float *P,
+                                                   const GemmArgs &a, int f, int n0) {
+  using TL = Tile<BM, BN, WM, WN, NST>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN, r16 = lane & 15, g = lane >> 4;
+  constexpr int HB = BM / 2;
+#pragma unroll
+  for (int j = 0; j < TL::FN; ++j) {
+    const int tok = n0 + wn * TL::TN + j * 16 + r16;
+    if (tok >= a.T) continue;
+    float *prow = P + static_cast<size_t>(tok) * a.M;
+#pragma unroll
+    for (int i = 0; i < TL::FM; ++i) {
+      const int v = wm * TL::TM + i * 16 + g * 4;
+      const int row = a.pair ? (v >= HB ? a.pair : 0) + f * HB + (v & (HB - 1)) : f * BM + v;
+      const int lim = a.pair ? a.pair - (f * HB + (v & (HB - 1))) : a.M - (f * BM + v);
+      const int nv = max(0, min(4, lim));
+      if (nv == 4 && ((a.M | row) & 3) == 0) {
+        *reinterpret_cast<f32x4 *>(prow + row) = acc[i][j];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < nv) prow[row + e] = acc[i][j][e];
+      }
+    }
+  }
+}
+
 // At most two waves per SIMD (the LDS ring allows one workgroup per CU for
 // the big tiles), so the compiler may use up to 256 VGPRs per lane.
 template <int BM, int BN, int WM, int WN, int NST>
@@ -238,19 +271,12 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, g = lane >> 4;
   const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lrow & 7);
-  // units: the K slices of every tile first (XCD-major), then the delta
-  // slices (short; they run on the CUs that the K slices leave free or free up)
+  // units: the K slices of every tile (XCD-major); on a split GEMM the last
+  // slice of a tile also computes the delta, so its K range is shorter by
+  // the delta's steps and every unit has about the same work
   int f, sl, t;
   const int nslices = a.mode == kPartial ? a.ksplit : 1;
-  const int main_units = a.nM * a.nT * nslices;
-  if (static_cast<int>(blockIdx.x) < main_units) {
-    unit_of(blockIdx.x, main_units, a.nT, nslices, f, sl, t);
-  } else {
-    const int u = blockIdx.x - main_units;
-    f = u / a.nT;
-    t = u % a.nT;
-    sl = a.ksplit;
-  }
+  unit_of(blockIdx.x, a.nM * a.nT * nslices, a.nT, nslices, f, sl, t);
   const int n0 = t * BN;
   // Tile rows.  Plain: rows f*BM + v.  Paired (gate|up with the activation
   // fused): v < BM/2 is gate row f*BM/2 + v and v >= BM/2 is up row
@@ -272,8 +298,7 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
     for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bool delta_slice = a.mode == kPartial && sl == a.ksplit;
-  if (!delta_slice) {
+  {
     // main segment (this workgroup's K slice): rows of A (features) then of B (tokens)
     const uint16_t *rp[TL::LPW];
 #pragma unroll
@@ -290,6 +315,19 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 
     const int nsteps = (a.K + kBK - 1) / kBK;
     const int sb = min(nsteps, sl * a.steps_per_slice), se = min(nsteps, sb + a.steps_per_slice);
     segment<BM, BN, WM, WN, NST>(acc, rp, a.K, sb, se, a.zero_row, lds);
+  }
+
+  // A split GEMM's unit stores its fp32 partial; the last slice of a tile
+  // then computes the delta into a zeroed accumulator and stores it as
+  // partial ksplit.
+  const bool delta_slice = a.mode == kPartial && sl == a.ksplit - 1 && a.nchild > 0;
+  if (a.mode == kPartial) {
+    store_partial_tile<BM, BN, WM, WN, NST>(acc, a.P + static_cast<size_t>(sl) * a.T * a.M, a, f, n0);
+    if (!delta_slice) return;
+#pragma unroll
+    for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const bool fused = a.mode == kFused || a.mode == kFusedAct;
@@ -331,27 +369,8 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 
     }
   }
 
-  // lane holds tile rows v = wm*TM + 16i + 4g + e, token n0 + wn*TN + 16j + r16
-  if (a.mode == kPartial) {
-    float *P = a.P + static_cast<size_t>(sl) * a.T * a.M;
-#pragma unroll
-    for (int j = 0; j < TL::FN; ++j) {
-      const int tok = n0 + wn * TL::TN + j * 16 + r16;
-      if (tok >= a.T) continue;
-      float *prow = P + static_cast<size_t>(tok) * a.M;
-#pragma unroll
-      for (int i = 0; i < TL::FM; ++i) {
-        const int v = wm * TL::TM + i * 16 + g * 4;
-        const int nv = nvalid(v, 4), row = actual(v);
-        if (nv == 4 && ((a.M | row) & 3) == 0) {
-          *reinterpret_cast<f32x4 *>(prow + row) = acc[i][j];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (e < nv) prow[row + e] = acc[i][j][e];
-        }
-      }
-    }
+  if (delta_slice) {
+    store_partial_tile<BM, BN, WM, WN, NST>(acc, a.P + static_cast<size_t>(a.ksplit) * a.T * a.M, a, f, n0);
     return;
   }
 
@@ -547,7 +566,7 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int units = a.nM * a.nT * (a.mode == kPartial ? a.ksplit + (a.nchild > 0 ? 1 : 0) : 1);
+  const int units = a.nM * a.nT * (a.mode == kPartial ? a.ksplit : 1);
   hipLaunchKernelGGL(kern, dim3(units), dim3(WM * WN * 64), TL::LDS, stream, a);
   return hipGetLastError();
 }
@@ -570,8 +589,9 @@ struct Plan {
 // estimated makespan -- rounds of workgroups over the CUs times the work of
 // one workgroup, scaled by the tile's efficiency -- plus, when K is split, the
 // cost of writing and re-reading the fp32 partials and of the finish launch.
-// A split GEMM runs the delta as one short extra slice per tile, which fills
-// in behind the K slices.  Unit: one 64-k step of a 256 x 128 tile (48 KB
+// On a split GEMM the last slice of a tile also runs the delta: the slices
+// split the K steps plus the delta steps evenly, the last one taking that
+// many fewer K steps.  Unit: one 64-k step of a 256 x 128 tile (48 KB
 // streamed per CU).
 Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true) {
   const int nsteps = (K + kBK - 1) / kBK;
@@ -583,15 +603,20 @@ Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true) {
     const double scale = (kTiles[i].BM * kTiles[i].BN) / (256.0 * 128.0) / kTiles[i].eff;
     const int max_split = allow_split ? std::min(kMaxSplit, std::max(1, nsteps / kMinSliceSteps)) : 1;
     for (int ks = 1; ks <= max_split; ++ks) {
-      const int per = (nsteps + ks - 1) / ks;
-      if (nsteps > 0 && (nsteps + per - 1) / per != ks) continue;  // some slice would be empty
+      const int work = ks == 1 ? nsteps : nsteps + dsteps;  // steps one tile's slices share
+      const int per = (work + ks - 1) / ks;
+      // every slice but the last takes per K steps; the last takes the rest
+      // of K (possibly none) and the delta
+      if (ks > 1) {
+        const int last_k = nsteps - (ks - 1) * per;
+        if (last_k < 0 || (last_k == 0 && dsteps == 0)) continue;  // a slice would be empty
+      }
       const long rounds = (tiles * ks + kCUs - 1) / kCUs;
       double cost;
       if (ks == 1) {
         cost = static_cast<double>(rounds) * (per + dsteps) * scale;
       } else {
-        const double total = static_cast<double>(tiles) * (static_cast<double>(ks) * per + dsteps) / kCUs;
-        cost = std::max(static_cast<double>(rounds) * per, total) * scale;
+        cost = static_cast<double>(rounds) * per * scale;
         cost += 2.0 * (ks + (dsteps > 0 ? 1 : 0)) * static_cast<double>(T) * M * 4 / (kCUs * 48.0 * 1024) + 8.0;
       }
       if (cost < best_cost) {
@@ -695,7 +720,8 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const 
     a.mode = act >= 0 ? kFusedAct : kFused;
     return launch_planned(a, p, stream);
   }
-  // K slices plus (if any child has a rank) one delta slice per tile
+  // K slices; the last slice of each tile also computes the delta (if any
+  // child has a rank) into its own partial
   const bool any_rank = delta_steps(c) > 0;
   if (!any_rank) a.nchild = 0;
   a.mode = kPartial;
