@@ -41,9 +41,12 @@ def call(b, layer, c, x):
     return b.stacked(layer, c, x) if c in ("qkv", "gate_up") else b.linear(layer, c, x)
 
 
-@pytest.mark.parametrize("rank", [0, 5, 64])
+@pytest.mark.parametrize("rank", [0, 5, 64, 100])
 @pytest.mark.parametrize("T", [1, 5, 16, 17, 40])
 def test_ragged_shapes(gpu_lib, rank, T):
+    """Against the oracle: decode (T <= 16) and prefill (T > 16) on ragged
+    rows, K tails and ranks 0, 5, 64 and 100 (padded to 128: several rank
+    steps per epilogue wave)."""
     wl = ragged(rank)
     ow = OracleWorkload(wl, DEV)
     b = sdev.load(wl, DEV)
