@@ -61,7 +61,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBK = 64;         // k per stage
 constexpr int kRowBytes = 128;  // kBK bf16 per LDS row
-constexpr int kMinSliceSteps = 8;
+constexpr int kMinSliceSteps = 4;
+// A 64-k step of any tile costs at least this (in units of a 256 x 128 step
+// at full streaming rate): with few workgroups per CU a step waits out the
+// memory latency of its loads rather than the stream rate.
+constexpr double kStepFloor = 0.55;
+// Cost (same units) of the extra launch that sums split-K partials.
+constexpr double kSplitLaunch = 4.0;
 constexpr int kMaxSplit = 16;
 constexpr int kCUs = 256;
 
@@ -597,10 +603,13 @@ Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true) {
   const int nsteps = (K + kBK - 1) / kBK;
   Plan best{kNumTiles - 1, 1, nsteps, (M + 63) / 64, (T + 63) / 64};
   double best_cost = 1e300;
-  for (int i = 0; i < kNumTiles; ++i) {
+  // smallest tile first: on equal cost (latency-bound small GEMMs) the tile
+  // that wastes no rows wins
+  for (int i = kNumTiles - 1; i >= 0; --i) {
+    if (i != kNumTiles - 1 && kTiles[i].BM >= 2 * M) continue;  // at least half the rows would be empty
     const int nM = (M + kTiles[i].BM - 1) / kTiles[i].BM, nT = (T + kTiles[i].BN - 1) / kTiles[i].BN;
     const long tiles = static_cast<long>(nM) * nT;
-    const double scale = (kTiles[i].BM * kTiles[i].BN) / (256.0 * 128.0) / kTiles[i].eff;
+    const double scale = std::max(kStepFloor, (kTiles[i].BM * kTiles[i].BN) / (256.0 * 128.0) / kTiles[i].eff);
     const int max_split = allow_split ? std::min(kMaxSplit, std::max(1, nsteps / kMinSliceSteps)) : 1;
     for (int ks = 1; ks <= max_split; ++ks) {
       const int work = ks == 1 ? nsteps : nsteps + dsteps;  // steps one tile's slices share
@@ -617,7 +626,7 @@ Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true) {
         cost = static_cast<double>(rounds) * (per + dsteps) * scale;
       } else {
         cost = static_cast<double>(rounds) * per * scale;
-        cost += 2.0 * (ks + (dsteps > 0 ? 1 : 0)) * static_cast<double>(T) * M * 4 / (kCUs * 48.0 * 1024) + 8.0;
+        cost += 2.0 * (ks + (dsteps > 0 ? 1 : 0)) * static_cast<double>(T) * M * 4 / (kCUs * 48.0 * 1024) + kSplitLaunch;
       }
       if (cost < best_cost) {
         best_cost = cost;
