@@ -80,6 +80,10 @@ class Step:
         import torch
         self.items = []
         self.bytes_rd = 0
+        # the same bytes with each band's W0 counted once for the step (the
+        # floor if every re-read of a band-shared W0 hit a cache)
+        self.bytes_band_unique = 0
+        seen_w0 = set()
         self.bytes_wr = 0
         self.flops = 0
         self.per_call = {}
@@ -95,6 +99,15 @@ class Step:
                 fl = call_flops(wl, layer, fams_here, T)
                 self.items.append((layer, name, stacked, x, y))
                 self.bytes_rd += rd
+                self.bytes_band_unique += rd
+                for f in fams_here:
+                    if not wl.has(lt, f):
+                        continue
+                    key = (wl.band(layer), 0 if f in ("gate", "up", "down") else lt, f)
+                    if key in seen_w0:
+                        N, K = wl.shape(lt, f)
+                        self.bytes_band_unique -= N * K + 4 * N if w0_format == "fp8" else 2 * N * K
+                    seen_w0.add(key)
                 self.bytes_wr += wr
                 self.flops += fl
                 pc = self.per_call.setdefault(name, {"calls": 0, "bytes": 0, "flops": 0})
@@ -204,6 +217,7 @@ def decode_section(wl, T, steps, warmup, dev, reps=3, w0_format="bf16"):
     kern_time = sum(durs[n] * pc["calls"] for n, pc in step.per_call.items())
     out = {"step_s": t_step, "bytes_read": step.bytes_rd, "bytes_written": step.bytes_wr,
            "GBps": step.bytes_rd / t_step / 1e9, "launches": launches,
+           "bytes_band_unique": step.bytes_band_unique, "GBps_band_unique": step.bytes_band_unique / t_step / 1e9,
            "kernel_GBps": step.bytes_rd / kern_time / 1e9,
            "avg_launch_us": kern_time / launches * 1e6, "bytes_per_launch": step.bytes_rd / launches,
            "per_call": per_call}
