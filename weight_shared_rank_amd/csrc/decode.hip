@@ -54,6 +54,12 @@ namespace {
 #ifndef WL_DECODE_TARGET_WGS
 #define WL_DECODE_TARGET_WGS 4096
 #endif
+#ifndef WL_STREAM_ROWS
+#define WL_STREAM_ROWS 2
+#endif
+#ifndef WL_STREAM_ROWS_MIN_T
+#define WL_STREAM_ROWS_MIN_T 2
+#endif
 #ifndef WL_FP8_UNROLL
 #define WL_FP8_UNROLL 2
 #endif
@@ -63,6 +69,8 @@ namespace {
 constexpr int kStreamWaves = WL_STREAM_WAVES;
 constexpr int kStreamUnroll = WL_STREAM_UNROLL;
 constexpr int kEpiWaves = WL_EPI_WAVES;
+constexpr int kStreamRows = WL_STREAM_ROWS;         // row tiles per stream workgroup for T >= kStreamRowsMinT
+constexpr int kStreamRowsMinT = WL_STREAM_ROWS_MIN_T;
 constexpr int kTargetWgs = WL_DECODE_TARGET_WGS;
 constexpr int kFp8Unroll = WL_FP8_UNROLL;
 
@@ -214,6 +222,114 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = row0 + g * 4 + i;
+    if (row < nrows) dst[row] = tot[i];
+  }
+}
+
+// The stream launch for several tokens (bf16 W0): like stream_kernel, but a
+// workgroup owns R consecutive 16-row tiles and every wave multiplies each x
+// fragment it loads into all R of them.  With T > 1 the x fragments are real
+// rows (16 cache lines a load, as many as a W0 fragment), and loading them
+// once per R row blocks cuts the operand traffic into the CU from 2x to
+// (1 + 1/R)x the W0 bytes.  Waves 0..R-1 each reduce one tile.
+template <int W, int UNROLL, int R>
+__global__ __launch_bounds__(W * 64) void stream_rows_kernel(CallDesc c, float *p_part, uint16_t *z_pair,
+                                                             int ntile_vt, int KS) {
+  static_assert(W >= R, "one reducing wave per tile");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const bool vt = static_cast<int>(blockIdx.x) < ntile_vt;
+  const int widx = blockIdx.x - ntile_vt;
+  // V^T tiles (full K) stay 16 rows; W0 workgroups own R tiles
+  const int row0 = vt ? blockIdx.x * 16 : (widx / KS) * 16 * R;
+  const int nb = vt ? 1 : R;  // tiles of this workgroup
+  const int slice = vt ? 0 : widx % KS;
+  const int nslices = vt ? 1 : KS;
+  const uint16_t *mat = vt ? c.Vt : c.W0;
+  const int nrows = vt ? c.Rz : c.Ntot;
+  const int K = c.K;
+  const int nsteps = (K + 31) >> 5;
+  const int per = (nsteps + nslices - 1) / nslices;
+  const int s_begin = min(nsteps, slice * per), s_end = min(nsteps, s_begin + per);
+
+  // Rows past the end read the workgroup's first row (always valid); their
+  // results are never stored.  Token columns >= T are zero.
+  const bool tok_ok = r16 < c.T;
+  const uint16_t *xrow = c.x + static_cast<size_t>(tok_ok ? r16 : 0) * K + g * 8;
+  const uint16_t *arow[R];
+#pragma unroll
+  for (int b = 0; b < R; ++b) {
+    const int r = row0 + 16 * b + r16;
+    arow[b] = mat + static_cast<size_t>(r < nrows ? r : row0) * K + g * 8;
+  }
+  f32x4 acc[R];
+#pragma unroll
+  for (int b = 0; b < R; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const int nfull_end = min(s_end, K >> 5);  // steps entirely inside K
+  const int nblocks = max(0, nfull_end - s_begin) / UNROLL;
+  for (int bk = wave; bk < nblocks; bk += W) {
+    const int s0 = s_begin + bk * UNROLL;
+    u32x4 a[R][UNROLL], xb[UNROLL];
+#pragma unroll
+    for (int b = 0; b < R; ++b)
+      if (b < nb) {
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) a[b][j] = ld16(arow[b] + (s0 + j) * 32);
+      }
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      // unconditional load (row clamped to a valid one), then select
+      const u32x4 v = ld16(xrow + (s0 + j) * 32);
+      xb[j] = tok_ok ? v : zero4;
+    }
+#pragma unroll
+    for (int b = 0; b < R; ++b)
+      if (b < nb) {
+#pragma unroll
+        for (int j = 0; j < UNROLL; ++j) acc[b] = mfma16x16x32(a[b][j], xb[j], acc[b]);
+      }
+  }
+  for (int s = s_begin + nblocks * UNROLL + wave; s < s_end; s += W) {
+    const bool kin = s * 32 + g * 8 < K;  // the last step may be partial
+    const u32x4 v = kin ? ld16(xrow + s * 32) : zero4;
+#pragma unroll
+    for (int b = 0; b < R; ++b)
+      if (b < nb) {
+        const u32x4 a = kin ? ld16(arow[b] + s * 32) : zero4;
+        acc[b] = mfma16x16x32(a, tok_ok ? v : zero4, acc[b]);
+      }
+  }
+
+  __shared__ f32x4 red[W][R][64];
+#pragma unroll
+  for (int b = 0; b < R; ++b) red[wave][b][lane] = acc[b];
+  __syncthreads();
+  if (wave >= nb || !tok_ok) return;
+  const int b = wave;  // this wave reduces tile b (waves in a fixed order)
+  f32x4 tot = red[0][b][lane];
+#pragma unroll
+  for (int w = 1; w < W; ++w) tot += red[w][b][lane];
+  const int tile0 = row0 + 16 * b;
+  // lane holds D[m = 4g + i][n = r16]: rows tile0 + 4g + i, token r16
+  if (vt) {
+    uint16_t *zh = z_pair + static_cast<size_t>(r16) * c.Rz;
+    uint16_t *zl = zh + static_cast<size_t>(c.T) * c.Rz;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile0 + g * 4 + i;
+      if (row < nrows) {
+        const uint16_t hi = f32_to_bf16(tot[i]);
+        zh[row] = hi;
+        zl[row] = f32_to_bf16(tot[i] - bf16_to_f32(hi));
+      }
+    }
+    return;
+  }
+  float *dst = p_part + (static_cast<size_t>(slice) * c.T + r16) * c.Ntot;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = tile0 + g * 4 + i;
     if (row < nrows) dst[row] = tot[i];
   }
 }
@@ -416,10 +532,23 @@ int decode_k_slices(int Ntot, int Rz, int K) {
 
 hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream, int act,
                          uint16_t *h, int ldh) {
-  const int KS = c.W0f8 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV) : decode_k_slices(c.Ntot, c.Rz, c.K);
-  const int nt_w0 = (c.Ntot + 15) / 16, nt_vt = (c.Rz + 15) / 16;
-  hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nt_vt + nt_w0 * KS), dim3(kStreamWaves * 64),
-                     0, stream, c, p_part, z_pair, nt_vt, KS);
+  const int nt_w0 = (c.Ntot + 15) / 16;
+  int KS;
+  const int KS1 = decode_k_slices(c.Ntot, c.Rz, c.K);
+  constexpr int R = kStreamRows;
+  if (c.W0f8 == nullptr && c.T >= kStreamRowsMinT && KS1 * R <= kDecodeMaxSlices) {
+    // several tokens: R row tiles per W0 workgroup share each x fragment;
+    // R times the K slices keep the workgroup count (and the bytes in flight)
+    KS = KS1 * R;
+    const int nw_w0 = (c.Ntot + 16 * R - 1) / (16 * R), nt_vt = (c.Rz + 15) / 16;
+    hipLaunchKernelGGL((stream_rows_kernel<kStreamWaves, kStreamUnroll, R>), dim3(nt_vt + nw_w0 * KS),
+                       dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
+  } else {
+    KS = c.W0f8 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV) : decode_k_slices(c.Ntot, c.Rz, c.K);
+    const int nt_vt = (c.Rz + 15) / 16;
+    hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nt_vt + nt_w0 * KS),
+                       dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (act < 0) {
