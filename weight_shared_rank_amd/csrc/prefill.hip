@@ -222,6 +222,92 @@ __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16]
   __builtin_amdgcn_s_barrier();
 }
 
+// The two deltas of a paired gate|up tile in one pass.  Tile rows v < BM/2
+// are gate rows (A = U_gate rows, B = the Z_gate columns) and v >= BM/2 the
+// matching up rows (U_up, Z_up); a stage holds both B blocks, so every wave
+// multiplies only its own child's rows, where two separate segments would
+// each run half the tile on zero rows.  Two 64-k stages of BM + 2 BN rows in
+// the ring (which has room for them for every tile shape).  Rank steps past
+// a child's padded rank read the zero row.
+template <int BM, int BN, int WM, int WN, int NST>
+__device__ __forceinline__ void paired_delta(f32x4 (&acc)[BM / WM / 16][BN / WN / 16], const GemmArgs &a, int f,
+                                             int n0, uint8_t *lds) {
+  using TL = Tile<BM, BN, WM, WN, NST>;
+  constexpr int HB = BM / 2;
+  constexpr int GA = BM / 8, GB2 = 2 * BN / 8;  // 8-row load groups: A, then both B blocks
+  constexpr int LPW2 = (GA + GB2) / TL::NW;
+  constexpr int STAGE2 = (BM + 2 * BN) * kRowBytes;
+  static_assert((GA + GB2) % TL::NW == 0, "8-row groups must split evenly over the waves");
+  static_assert(2 * STAGE2 <= TL::LDS, "two paired-delta stages must fit the ring");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lrow & 7);
+  const ChildDesc &cg = a.ch[0], &cu = a.ch[1];
+  const int nsteps = (max(cg.rpad, cu.rpad) + kBK - 1) / kBK;
+  const uint16_t *rp[LPW2];
+  int klen[LPW2], ldsoff[LPW2];
+#pragma unroll
+  for (int q = 0; q < LPW2; ++q) {
+    const int gq = wave * LPW2 + q;
+    if (gq < GA) {
+      const int v = gq * 8 + lrow;
+      const bool up = v >= HB;
+      const ChildDesc &ch = up ? cu : cg;
+      const int j = f * HB + (v & (HB - 1));
+      rp[q] = j < a.pair ? ch.U + static_cast<int64_t>(j) * ch.rpad + lchunk * 8 : nullptr;
+      klen[q] = ch.rpad;
+      ldsoff[q] = gq * 1024;
+    } else {
+      const int gb = gq - GA, up = gb >= BN / 8;
+      const ChildDesc &ch = up ? cu : cg;
+      const int row = n0 + (gb - (up ? BN / 8 : 0)) * 8 + lrow;
+      rp[q] = row < a.T ? a.Z + static_cast<int64_t>(row) * a.ldz + ch.zoff + lchunk * 8 : nullptr;
+      klen[q] = ch.rpad;
+      ldsoff[q] = BM * kRowBytes + gb * 1024;
+    }
+  }
+  auto issue = [&](int stage, int step) __attribute__((always_inline)) {
+    const int k = step * kBK + lchunk * 8;
+#pragma unroll
+    for (int q = 0; q < LPW2; ++q) {
+      const uint16_t *src = (rp[q] != nullptr && k < klen[q]) ? rp[q] + step * kBK : a.zero_row;
+      __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                       (lds_void *)(lds + stage * STAGE2 + ldsoff[q]), 16, 0, 0);
+    }
+  };
+  const int arow = (wm * TL::TM + r16) * kRowBytes;
+  const int region = wm * TL::TM < HB ? 0 : 1;  // gate waves read Z_gate, up waves Z_up
+  const int brow = (BM + region * BN + wn * TL::TN + r16) * kRowBytes;
+  const int sw0 = ((0 + g) ^ (r16 & 7)) * 16, sw1 = ((4 + g) ^ (r16 & 7)) * 16;
+  if (nsteps > 0) issue(0, 0);
+  for (int kt = 0; kt < nsteps; ++kt) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // stage kt visible; stage kt-1 no longer read
+    if (kt + 1 < nsteps) issue((kt + 1) & 1, kt + 1);
+    const uint8_t *sb = lds + (kt & 1) * STAGE2;
+    u32x4 fa[2][TL::FM], fb[2][TL::FN];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int sw = h ? sw1 : sw0;
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i)
+        fa[h][i] = *reinterpret_cast<const u32x4 *>(sb + arow + i * 16 * kRowBytes + sw);
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j)
+        fb[h][j] = *reinterpret_cast<const u32x4 *>(sb + brow + j * 16 * kRowBytes + sw);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[h][i], fb[h][j], acc[i][j]);
+  }
+  // every wave is done with the ring before it is refilled
+  __builtin_amdgcn_s_barrier();
+}
+
 // Workgroup index -> (feature tile, K slice, token tile), XCD-major: hardware
 // sends workgroup w to XCD w % 8; XCD x is given the contiguous unit range
 // [x * per + min(x, rem), ...) of the total units, token tile fastest.
@@ -269,7 +355,10 @@ __device__ __forceinline__ void store_partial_tile(const f32x4 (&acc)[BM / WM / 
 
 // At most two waves per SIMD (the LDS ring allows one workgroup per CU for
 // the big tiles), so the compiler may use up to 256 VGPRs per lane.
-template <int BM, int BN, int WM, int WN, int NST>
+// PAIRED: the instantiation for paired gate|up calls (rows of a tile split
+// between the two children), which runs both deltas in one pass; the
+// others never contain that code, so their register allocation is their own.
+template <int BM, int BN, int WM, int WN, int NST, bool PAIRED>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmArgs a) {
   using TL = Tile<BM, BN, WM, WN, NST>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -351,7 +440,10 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 
       }
     }
   }
-  if (fused || delta_slice) {
+  if (PAIRED && (fused || delta_slice)) {
+    // paired gate|up tile: both deltas in one pass
+    if constexpr (PAIRED) paired_delta<BM, BN, WM, WN, NST>(acc, a, f, n0, lds);
+  } else if (fused || delta_slice) {
     // delta = Z U^T for every child with rows in this tile
     for (int ci = 0; ci < a.nchild; ++ci) {
       const ChildDesc &ch = a.ch[ci];
@@ -561,10 +653,10 @@ __global__ void finish_kernel(FinishArgs a) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NST>
-hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
+template <int BM, int BN, int WM, int WN, int NST, bool PAIRED>
+hipError_t launch_gemm_inst(const GemmArgs &a, hipStream_t stream) {
   using TL = Tile<BM, BN, WM, WN, NST>;
-  auto kern = gemm_kernel<BM, BN, WM, WN, NST>;
+  auto kern = gemm_kernel<BM, BN, WM, WN, NST, PAIRED>;
   static bool attr_set = false;  // per instance; setting it twice is harmless
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -575,6 +667,12 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
   const int units = a.nM * a.nT * (a.mode == kPartial ? a.ksplit : 1);
   hipLaunchKernelGGL(kern, dim3(units), dim3(WM * WN * 64), TL::LDS, stream, a);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int NST>
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
+  return (a.pair && a.nchild == 2) ? launch_gemm_inst<BM, BN, WM, WN, NST, true>(a, stream)
+                                   : launch_gemm_inst<BM, BN, WM, WN, NST, false>(a, stream);
 }
 
 // Tile shapes: BM features x BN tokens.  eff ranks the shapes by measured
