@@ -106,6 +106,21 @@ def test_determinism_and_t0(gpu_lib):
         assert torch.equal(y1, y2)
     y = torch.full((0, 4096), 7, dtype=torch.bfloat16, device=DEV)
     b.linear(0, "up", torch.empty((0, 1152), dtype=torch.bfloat16, device=DEV), y=y)
+    # stacked calls (decode with two-tile stream workgroups, prefill) and the
+    # paired gate|up activation kernel repeat bit for bit too
+    wr = ragged(64)
+    br = sdev.load(wr, DEV)
+    for T in (16, 200):
+        for c in ("qkv", "gate_up"):
+            x = wr.x(0, c, T, DEV)
+            announce(f"determinism stacked {c} T={T}")
+            y1, y2 = br.stacked(0, c, x), br.stacked(0, c, x)
+            torch.cuda.synchronize()
+            assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), (c, T)
+        x = wr.x(0, "gate_up", T, DEV)
+        h1, h2 = br.gate_up_act(0, "gelu_tanh", x), br.gate_up_act(0, "gelu_tanh", x)
+        torch.cuda.synchronize()
+        assert torch.equal(h1.view(torch.int16), h2.view(torch.int16)), ("act", T)
 
 
 def test_workspace_too_small_and_aliasing(gpu_lib):
