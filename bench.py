@@ -11,7 +11,8 @@ The same run also times
   * the Gemma-3-1B-shaped decode step (G=13, r=32, T=1),
   * prefill steps (MFMA path): Gemma-4-31B mixed attention (10 full + 50
     sliding layers, G=1 per type, r=1024, T=512) and Gemma-3-1B (G=1, r=64,
-    T=2048, 7 single-family calls per layer), in TFLOP/s,
+    T=2048, 7 single-family calls per layer; and, as a secondary figure, the
+    same layers as 4 calls with q|k|v and gate|up stacked), in TFLOP/s,
   * per-launch kernel durations with HIP events on the launch stream (the
     roofline figure), and
   * the fp64 CPU oracle on a bounded sample of the headline workload,
@@ -644,6 +645,9 @@ def main():
         singles = tuple((f, (f,)) for f in synth.FAMILIES)
         res["prefill3"] = prefill_section(synth.workload(3), 2048, singles, args.steps, args.warmup, dev)
         log(f"prefill w3: {res['prefill3']['TFLOPs']:.1f} TFLOP/s")
+        # secondary: the same layers with q|k|v and gate|up as stacked calls (4 calls per layer instead of 7)
+        res["prefill3_stacked"] = prefill_section(synth.workload(3), 2048, CALLS, args.steps, args.warmup, dev)
+        log(f"prefill w3, stacked calls: {res['prefill3_stacked']['TFLOPs']:.1f} TFLOP/s")
 
     if args.only in ("all", "decompose"):
         res["decompose_gemma3"] = decompose_section(dev, cpu_budget=0.0 if args.no_cpu else 4.0)
@@ -688,6 +692,8 @@ def main():
                                         "traffic": traffic_from_profile("prefill", psha), "source_sha": psha}}
         if "prefill3" in res:
             line["prefill"]["gemma3_1b_T2048_TFLOPs"] = round(res["prefill3"]["TFLOPs"], 2)
+        if "prefill3_stacked" in res:
+            line["prefill"]["gemma3_1b_T2048_stacked_TFLOPs"] = round(res["prefill3_stacked"]["TFLOPs"], 2)
     if not args.no_cpu and args.only in ("all", "decode"):
         log("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(wl4, 1, args.cpu_budget, dev)
