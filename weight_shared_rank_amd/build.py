@@ -50,5 +50,35 @@ def build(verbose=True, extra_flags=()):
     return LIB
 
 
+def asan_runtime():
+    """Path of the clang AddressSanitizer runtime that a host-sanitized
+    library needs preloaded into the (uninstrumented) Python process."""
+    import glob
+    found = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang", "*",
+                                          "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    return found[-1] if found else None
+
+
+def build_host_sanitized(verbose=False):
+    """A copy of the library whose host code (the C ABI, the planners, the
+    launchers, the decomposition driver) is built with AddressSanitizer and
+    UndefinedBehaviorSanitizer; device code is built as usual (no GPU
+    sanitizer).  Written to _build/asan/libweightless_asan.so; load it with
+    asan_runtime() preloaded.  For CPU tests of the host paths only."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = os.path.join(BUILD, "asan")
+    os.makedirs(out, exist_ok=True)
+    # host-side only: every sanitizer flag is preceded by -Xarch_host
+    san = [flag for kind in ("address", "undefined") for flag in ("-Xarch_host", "-fsanitize=" + kind)]
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", *san, "-Xarch_host", "-fno-omit-frame-pointer"]
+    objs = [os.path.join(out, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        list(ex.map(lambda so: _run([HIPCC, *flags, "-c", os.path.join(CSRC, so[0]), "-o", so[1]], verbose),
+                    zip(SOURCES, objs)))
+    lib = os.path.join(out, "libweightless_asan.so")
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *san, "-shared-libsan", *objs, "-o", lib], verbose)
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
