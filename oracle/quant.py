@@ -1,8 +1,8 @@
 """FP8 (OCP E4M3) shared block with per-row power-of-two scales, in fp64.
 
-SURVEY's NEXT row 4 reads the pages' quantized-shared-block headroom ("Quality
-(Gemma 4 31B)" page, "Verdict": trained sharing on 4-bit shared blocks) on
-this part's own 8-bit format.  A stored W0 row w (bf16 values) becomes codes
+This is the pages' quantized-shared-block headroom ("Quality (Gemma 4 31B)"
+page, "Verdict": trained sharing on 4-bit shared blocks) taken in this
+part's own 8-bit format.  A stored W0 row w (bf16 values) becomes codes
 c_j and one scale q = 2^e such that w_j ~= value(c_j) * q:
 
 * e is the smallest integer with max_j |w_j| <= 448 * 2^e (448 is the largest
