@@ -160,3 +160,33 @@ def test_decompose_rejects_bad_arguments(gpu_lib):
         binding.decompose(w, 17, synth.sketch_matrix(1, 16, 16, DEV))  # rank > min(N, K)
     with pytest.raises(binding.WlError):
         binding.decompose(w, 4, synth.sketch_matrix(1, 16, 3, DEV))  # wrong sketch width
+
+
+def test_concurrent_calls_match_sequential(gpu_lib):
+    """Independent band calls on several streams from several host threads
+    (each with its own workspace) give the same bits as one call at a time:
+    a call's state lives in its arguments and workspace only."""
+    from concurrent.futures import ThreadPoolExecutor
+    announce("decompose: 6 bands on 3 streams against one at a time")
+    rank, n, k = 8, 192, 136
+    l = binding.sketch_columns(n, k, rank, 16)
+    bands = [(synth.band_layers(81 + i, 2, n, k, planted_rank=3).to(DEV), synth.sketch_matrix(90 + i, k, l, DEV))
+             for i in range(6)]
+    torch.cuda.synchronize()
+    seq = [binding.decompose(w, rank, om) for w, om in bands]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+
+    def work(i):
+        with torch.cuda.stream(streams[i]):
+            out = [(j, binding.decompose(w, rank, om, stream=streams[i])) for j, (w, om) in enumerate(bands)
+                   if j % 3 == i]
+        streams[i].synchronize()
+        return out
+    with ThreadPoolExecutor(3) as ex:
+        par = dict(p for outs in ex.map(work, range(3)) for p in outs)
+    torch.cuda.synchronize()
+    for j, ref in enumerate(seq):
+        for a, b in zip(ref, par[j]):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), j

@@ -117,17 +117,11 @@ struct Dev {
   hipError_t err = hipSuccess;
   float *part = nullptr;  // split-K partials of the fp32 GEMMs
   size_t part_elems = 0;
-  std::vector<float> up_u, up_v;  // host sources of in-flight uploads (alive until the next sync)
+  std::vector<float> up_t, up_u, up_v;  // host sources of in-flight uploads (alive until the next sync)
   bool ok() const { return err == hipSuccess; }
   hipError_t gemm(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn, float *C,
                   int64_t ldc, int M, int N, int K) {
     return wl::launch_gemm_f32(A, sam, sak, B, sbk, sbn, C, ldc, M, N, K, part, part_elems, s);
-  }
-  void put(float *d, const std::vector<double> &h) {
-    if (!ok()) return;
-    std::vector<float> f(h.begin(), h.end());
-    err = hipMemcpyAsync(d, f.data(), f.size() * 4, hipMemcpyHostToDevice, s);
-    if (ok()) err = hipStreamSynchronize(s);
   }
   // Asynchronous upload from a host vector that stays alive until the next sync.
   void put_async(float *d, std::vector<float> &keep, const std::vector<double> &h) {
@@ -168,7 +162,9 @@ Orth orthonormalize(Dev &d, float *&Y, float *&tmp, int n, int l, float *small, 
       good = cholesky(L, l);
     }
     if (!good) return kOrthFail;
-    d.put(small, inv_lower_transpose(L, l));
+    // the upload needs no wait: the product below is ordered after it on the
+    // stream, and the next get() synchronizes before up_t is reused
+    d.put_async(small, d.up_t, inv_lower_transpose(L, l));
     if (d.ok()) d.err = d.gemm(Y, l, 1, small, l, 1, tmp, l, n, l, l);  // Y T
     std::swap(Y, tmp);
   }
