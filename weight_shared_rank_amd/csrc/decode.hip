@@ -60,6 +60,9 @@ namespace {
 #ifndef WL_STREAM_ROWS_MIN_T
 #define WL_STREAM_ROWS_MIN_T 2
 #endif
+#ifndef WL_DECODE_TARGET_WGS_ROWS
+#define WL_DECODE_TARGET_WGS_ROWS 2048
+#endif
 #ifndef WL_FP8_UNROLL
 #define WL_FP8_UNROLL 2
 #endif
@@ -72,6 +75,9 @@ constexpr int kEpiWaves = WL_EPI_WAVES;
 constexpr int kStreamRows = WL_STREAM_ROWS;         // row tiles per stream workgroup for T >= kStreamRowsMinT
 constexpr int kStreamRowsMinT = WL_STREAM_ROWS_MIN_T;
 constexpr int kTargetWgs = WL_DECODE_TARGET_WGS;
+// K slices of the several-token path come from a lower workgroup target:
+// each slice writes a T-token-wide fp32 partial that the epilogue re-reads
+constexpr int kTargetWgsRows = WL_DECODE_TARGET_WGS_ROWS;
 constexpr int kFp8Unroll = WL_FP8_UNROLL;
 
 // One batch of UNROLL complete k-steps (32 k each): loads first, then MFMAs.
@@ -520,15 +526,19 @@ __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const
 
 }  // namespace
 
-int decode_k_slices(int Ntot, int Rz, int K) {
-  // Aim for about kTargetWgs workgroups in the stream launch, with K slices
+namespace {
+int k_slices_for(int Ntot, int Rz, int K, int target) {
+  // Aim for about `target` workgroups in the stream launch, with K slices
   // of at least 16 k-steps and at most kDecodeMaxSlices slices.
   const int tiles = (Ntot + 15) / 16 + (Rz + 15) / 16;
   const int nsteps = (K + 31) / 32;
-  int ks = (kTargetWgs + tiles - 1) / max(1, tiles);
+  int ks = (target + tiles - 1) / max(1, tiles);
   ks = min(ks, max(1, nsteps / 16));
   return max(1, min(ks, kDecodeMaxSlices));
 }
+}  // namespace
+
+int decode_k_slices(int Ntot, int Rz, int K) { return k_slices_for(Ntot, Rz, K, kTargetWgs); }
 
 hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream, int act,
                          uint16_t *h, int ldh) {
@@ -537,9 +547,10 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hip
   const int KS1 = decode_k_slices(c.Ntot, c.Rz, c.K);
   constexpr int R = kStreamRows;
   if (c.W0f8 == nullptr && c.T >= kStreamRowsMinT && KS1 * R <= kDecodeMaxSlices) {
-    // several tokens: R row tiles per W0 workgroup share each x fragment;
-    // R times the K slices keep the workgroup count (and the bytes in flight)
-    KS = KS1 * R;
+    // several tokens: R row tiles per W0 workgroup share each x fragment,
+    // with R times the slices of the lower several-token target (never more
+    // than the R * KS1 <= kDecodeMaxSlices checked above)
+    KS = R * min(KS1, k_slices_for(c.Ntot, c.Rz, c.K, kTargetWgsRows));
     const int nw_w0 = (c.Ntot + 16 * R - 1) / (16 * R), nt_vt = (c.Rz + 15) / 16;
     hipLaunchKernelGGL((stream_rows_kernel<kStreamWaves, kStreamUnroll, R>), dim3(nt_vt + nw_w0 * KS),
                        dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
