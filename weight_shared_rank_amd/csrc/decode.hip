@@ -60,6 +60,9 @@ namespace {
 #ifndef WL_STREAM_ROWS_MIN_T
 #define WL_STREAM_ROWS_MIN_T 2
 #endif
+#ifndef WL_STREAM_WIDE_MIN_T
+#define WL_STREAM_WIDE_MIN_T 8
+#endif
 #ifndef WL_DECODE_TARGET_WGS_ROWS
 #define WL_DECODE_TARGET_WGS_ROWS 2048
 #endif
@@ -74,6 +77,7 @@ constexpr int kStreamUnroll = WL_STREAM_UNROLL;
 constexpr int kEpiWaves = WL_EPI_WAVES;
 constexpr int kStreamRows = WL_STREAM_ROWS;         // row tiles per stream workgroup for T >= kStreamRowsMinT
 constexpr int kStreamRowsMinT = WL_STREAM_ROWS_MIN_T;
+constexpr int kStreamWideMinT = WL_STREAM_WIDE_MIN_T;
 constexpr int kTargetWgs = WL_DECODE_TARGET_WGS;
 // K slices of the several-token path come from a lower workgroup target:
 // each slice writes a T-token-wide fp32 partial that the epilogue re-reads
@@ -554,6 +558,15 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hip
     const int nw_w0 = (c.Ntot + 16 * R - 1) / (16 * R), nt_vt = (c.Rz + 15) / 16;
     hipLaunchKernelGGL((stream_rows_kernel<kStreamWaves, kStreamUnroll, R>), dim3(nt_vt + nw_w0 * KS),
                        dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
+  } else if (c.W0f8 == nullptr && c.T >= kStreamWideMinT && KS1 == kDecodeMaxSlices &&
+             ((c.K + 31) / 32 + KS1 - 1) / KS1 >= 2 * kStreamWaves * kStreamUnroll) {
+    // several tokens, long K slices (down-shaped calls): the two-tile kernel
+    // with twice the waves, so the workgroups halve but the waves in flight do
+    // not, at the full slice count; every wave still gets a block of k-steps
+    KS = KS1;
+    const int nw_w0 = (c.Ntot + 16 * R - 1) / (16 * R), nt_vt = (c.Rz + 15) / 16;
+    hipLaunchKernelGGL((stream_rows_kernel<2 * kStreamWaves, kStreamUnroll, R>), dim3(nt_vt + nw_w0 * KS),
+                       dim3(2 * kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
   } else {
     KS = c.W0f8 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV) : decode_k_slices(c.Ntot, c.Rz, c.K);
     const int nt_vt = (c.Rz + 15) / 16;
