@@ -606,9 +606,17 @@ struct FinishArgs {
 __device__ __forceinline__ float finished(const FinishArgs &a, int tok, int r) {
   const size_t plane = static_cast<size_t>(a.T) * a.M;
   const float *p = a.P + static_cast<size_t>(tok) * a.M + r;
+  const float d = a.has_delta ? p[a.ksplit * plane] : 0.f;
   float acc = 0.f;
-  for (int s = 0; s < a.ksplit; ++s) acc += p[s * plane];
-  return a.s[r] * acc + (a.has_delta ? p[a.ksplit * plane] : 0.f);
+  for (int s0 = 0; s0 < a.ksplit; s0 += 4) {  // four loads in flight, summed in slice order
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = p[min(s0 + j, a.ksplit - 1) * plane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s0 + j < a.ksplit) acc += v[j];
+  }
+  return a.s[r] * acc + d;
 }
 
 // h[tok][j] = act(gate_j) * up_j for the paired gate|up call on the split path.
@@ -629,9 +637,18 @@ __global__ void finish_kernel(FinishArgs a) {
   const float *p = a.P + static_cast<size_t>(tok) * a.M + row;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
   if (row + 3 < a.M && (a.M & 3) == 0) {
-    for (int s = 0; s < a.ksplit; ++s) acc += *reinterpret_cast<const f32x4 *>(p + s * plane);
     if (a.has_delta) d = *reinterpret_cast<const f32x4 *>(p + a.ksplit * plane);
     sc = *reinterpret_cast<const f32x4 *>(a.s + row);
+    // four slices' loads in flight at a time (slices past the last re-read
+    // it and are dropped); summed in slice order
+    for (int s0 = 0; s0 < a.ksplit; s0 += 4) {
+      f32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const f32x4 *>(p + min(s0 + j, a.ksplit - 1) * plane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (s0 + j < a.ksplit) acc += v[j];
+    }
   } else {
     for (int e = 0; e < 4 && row + e < a.M; ++e) {
       for (int s = 0; s < a.ksplit; ++s) acc[e] += p[s * plane + e];
@@ -640,6 +657,23 @@ __global__ void finish_kernel(FinishArgs a) {
     }
   }
   uint16_t *yrow = a.Y + static_cast<size_t>(tok) * a.ldy;
+  {
+    // four rows of one child with 8-byte aligned destinations: one store each
+    int ci = 0;
+    while (ci + 1 < a.nchild && row >= a.ch[ci + 1].row_start) ++ci;
+    const ChildDesc &ch = a.ch[ci];
+    const int jj = row - ch.row_start;
+    uint16_t *y0 = yrow + ch.y_off + jj;
+    uint16_t *y1 = ch.dup_off >= 0 ? yrow + ch.dup_off + jj : y0;
+    if (jj + 3 < ch.N && ((reinterpret_cast<uintptr_t>(y0) | reinterpret_cast<uintptr_t>(y1)) & 7) == 0) {
+      u32x2 o;
+      o[0] = f32_to_bf16(sc[0] * acc[0] + d[0]) | (static_cast<uint32_t>(f32_to_bf16(sc[1] * acc[1] + d[1])) << 16);
+      o[1] = f32_to_bf16(sc[2] * acc[2] + d[2]) | (static_cast<uint32_t>(f32_to_bf16(sc[3] * acc[3] + d[3])) << 16);
+      *reinterpret_cast<u32x2 *>(y0) = o;
+      if (ch.dup_off >= 0) *reinterpret_cast<u32x2 *>(y1) = o;
+      return;
+    }
+  }
   for (int e = 0; e < 4; ++e) {
     const int r = row + e;
     if (r >= a.M) break;
