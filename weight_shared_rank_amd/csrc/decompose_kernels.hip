@@ -112,8 +112,17 @@ __global__ void reduce_kernel(const float *P, int splits, int M, int N, float *C
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t mn = static_cast<int64_t>(M) * N;
   if (i >= mn) return;
+  // eight slices' loads in flight at a time (slices past the last re-read it
+  // and are dropped); summed in slice order
   float acc = 0.f;
-  for (int z = 0; z < splits; ++z) acc += P[z * mn + i];
+  for (int z0 = 0; z0 < splits; z0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = P[min(z0 + j, splits - 1) * mn + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (z0 + j < splits) acc += v[j];
+  }
   C[(i / N) * ldc + i % N] = acc;
 }
 
