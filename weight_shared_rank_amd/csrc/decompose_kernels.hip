@@ -57,31 +57,51 @@ __global__ void scale_residual_kernel(const uint16_t *W, const uint16_t *W0, int
 }
 
 // C[M][N] = sum_k A(m, k) B(k, n), A(m, k) = A[m * sam + k * sak], B(k, n) =
-// B[k * sbk + n * sbn]; fp32, 64 x 64 tiles, 16 k per LDS tile, 256 threads
-// with 4 x 4 outputs each.  blockIdx.z takes the k range [z kc, (z+1) kc);
-// with gridDim.z > 1 each slice writes its own partial C_z at C + z M ldc and
-// reduce_kernel adds them in slice order (deterministic).  Tile loads walk
-// the operand's unit-stride index fastest (a_m_fast: sam == 1).
+// B[k * sbk + n * sbn]; fp32, 64 x 64 tiles, 32 k per LDS tile, 256 threads
+// with 4 x 4 outputs each.  The next tile's elements are loaded into
+// registers while the current one is multiplied, so a workgroup pays the load
+// latency once per tile pair rather than once per tile; products are summed
+// in k order.  blockIdx.z takes the k range [z kc, (z+1) kc); with gridDim.z
+// > 1 each slice writes its own partial C_z at C + z M ldc and reduce_kernel
+// adds them in slice order (deterministic).  Tile loads walk the operand's
+// unit-stride index fastest (a_m_fast: sam == 1).
+constexpr int kF32Kt = 32;
 __global__ void gemm_f32_kernel(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn,
                                 float *C, int64_t ldc, int M, int N, int K, int kc, int a_m_fast, int b_n_fast) {
-  __shared__ float As[16][65], Bs[16][65];
+  constexpr int EPT = kF32Kt * 64 / 256;  // elements of each operand per thread and tile
+  __shared__ float As[kF32Kt][65], Bs[kF32Kt][65];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int kbeg = blockIdx.z * kc, kend = min(K, kbeg + kc);
   C += static_cast<int64_t>(blockIdx.z) * M * ldc;
   float acc[4][4] = {};
-  for (int k0 = kbeg; k0 < kend; k0 += 16) {
-    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
-      const int kk = a_m_fast ? (e >> 6) : (e & 15), mm = a_m_fast ? (e & 63) : (e >> 4);
+  float ra[EPT], rb[EPT];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = threadIdx.x + q * 256;
+      const int kk = a_m_fast ? (e >> 6) : (e & (kF32Kt - 1)), mm = a_m_fast ? (e & 63) : (e / kF32Kt);
       const int gm = m0 + mm, gk = k0 + kk;
-      As[kk][mm] = (gm < M && gk < kend) ? A[gm * sam + gk * sak] : 0.f;
-      const int kb = b_n_fast ? (e >> 6) : (e & 15), nn = b_n_fast ? (e & 63) : (e >> 4);
+      ra[q] = (gm < M && gk < kend) ? A[gm * sam + gk * sak] : 0.f;
+      const int kb = b_n_fast ? (e >> 6) : (e & (kF32Kt - 1)), nn = b_n_fast ? (e & 63) : (e / kF32Kt);
       const int gn = n0 + nn, gk2 = k0 + kb;
-      Bs[kb][nn] = (gn < N && gk2 < kend) ? B[gk2 * sbk + gn * sbn] : 0.f;
+      rb[q] = (gn < N && gk2 < kend) ? B[gk2 * sbk + gn * sbn] : 0.f;
+    }
+  };
+  if (kbeg < kend) load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += kF32Kt) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = threadIdx.x + q * 256;
+      const int kk = a_m_fast ? (e >> 6) : (e & (kF32Kt - 1)), mm = a_m_fast ? (e & 63) : (e / kF32Kt);
+      As[kk][mm] = ra[q];
+      const int kb = b_n_fast ? (e >> 6) : (e & (kF32Kt - 1)), nn = b_n_fast ? (e & 63) : (e / kF32Kt);
+      Bs[kb][nn] = rb[q];
     }
     __syncthreads();
+    if (k0 + kF32Kt < kend) load(k0 + kF32Kt);  // in flight during the products below
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
+    for (int kk = 0; kk < kF32Kt; ++kk) {
       float a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
@@ -161,7 +181,7 @@ namespace {
 int split_chunk(int K, int &splits) {
   int kc = std::max(K, 1);
   if (splits > 1) {
-    kc = ((K + splits - 1) / splits + 15) / 16 * 16;
+    kc = ((K + splits - 1) / splits + kF32Kt - 1) / kF32Kt * kF32Kt;  // whole k tiles per slice
     splits = (K + kc - 1) / kc;
   }
   return kc;
