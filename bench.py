@@ -422,7 +422,7 @@ def decompose_flops(m, n, k, rank, over, q):
     return m * per
 
 
-def decompose_section(dev, rank=32, over=16, q=4, cpu_budget=0.0, streams=8):
+def decompose_section(dev, rank=32, over=16, q=4, cpu_budget=0.0, streams=16):
     """GPU decomposition of the Gemma-3-1B-shaped model: 26 layers in 13
     bands (two layers per band), 7 families, rank 32: 91 band decompositions
     (182 matrices) from seeded i.i.d. N(0, 1/in) bf16 layer weights already
