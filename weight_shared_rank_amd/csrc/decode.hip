@@ -428,6 +428,23 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
 
   // lane holds D[m = 4g + i][n = r16]: rows rbase + i, token r16
   uint16_t *yrow = c.y + static_cast<size_t>(r16) * c.ldy;
+  {
+    // four rows of one child with 8-byte aligned destinations: one store each
+    int ci = 0;
+    while (ci + 1 < c.nchild && rbase >= c.ch[ci + 1].row_start) ++ci;
+    const ChildDesc &ch = c.ch[ci];
+    const int j = rbase - ch.row_start;
+    uint16_t *y0 = yrow + ch.y_off + j;
+    uint16_t *y1 = ch.dup_off >= 0 ? yrow + ch.dup_off + j : y0;
+    if (j + 3 < ch.N && ((reinterpret_cast<uintptr_t>(y0) | reinterpret_cast<uintptr_t>(y1)) & 7) == 0) {
+      u32x2 o;
+      o[0] = f32_to_bf16(sc[0] * p[0] + d[0]) | (static_cast<uint32_t>(f32_to_bf16(sc[1] * p[1] + d[1])) << 16);
+      o[1] = f32_to_bf16(sc[2] * p[2] + d[2]) | (static_cast<uint32_t>(f32_to_bf16(sc[3] * p[3] + d[3])) << 16);
+      *reinterpret_cast<u32x2 *>(y0) = o;
+      if (ch.dup_off >= 0) *reinterpret_cast<u32x2 *>(y1) = o;
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = rbase + i;
