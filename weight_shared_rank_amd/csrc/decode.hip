@@ -538,9 +538,20 @@ __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const
     }
   }
   uint16_t *hrow = h + static_cast<size_t>(r16) * ldh;
+  const int jb = j0 + 4 * g;
+  if (jb + 3 < Ng && (reinterpret_cast<uintptr_t>(hrow + jb) & 7) == 0) {
+    // four values with one 8-byte store
+    u32x2 o;
+    o[0] = f32_to_bf16(activation(act, y[0][0]) * y[1][0]) |
+           (static_cast<uint32_t>(f32_to_bf16(activation(act, y[0][1]) * y[1][1])) << 16);
+    o[1] = f32_to_bf16(activation(act, y[0][2]) * y[1][2]) |
+           (static_cast<uint32_t>(f32_to_bf16(activation(act, y[0][3]) * y[1][3])) << 16);
+    *reinterpret_cast<u32x2 *>(hrow + jb) = o;
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int j = j0 + 4 * g + i;
+    const int j = jb + i;
     if (j < Ng) hrow[j] = f32_to_bf16(activation(act, y[0][i]) * y[1][i]);
   }
 }
