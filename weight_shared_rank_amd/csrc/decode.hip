@@ -337,9 +337,14 @@ __global__ __launch_bounds__(W * 64) void stream_rows_kernel(CallDesc c, float *
     return;
   }
   float *dst = p_part + (static_cast<size_t>(slice) * c.T + r16) * c.Ntot;
+  const int rb = tile0 + g * 4;
+  if (rb + 3 < nrows && ((reinterpret_cast<uintptr_t>(dst + rb)) & 15) == 0) {
+    *reinterpret_cast<f32x4 *>(dst + rb) = tot;  // four rows with one store
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = tile0 + g * 4 + i;
+    const int row = rb + i;
     if (row < nrows) dst[row] = tot[i];
   }
 }
