@@ -198,6 +198,26 @@ def test_workload4_sampled_layers(gpu_lib):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(900)
+def test_workload4_mid_token_counts(gpu_lib):
+    """Layer 0 at T = 4 and 8: the several-token decode paths at the real
+    shapes (two-tile stream workgroups for q|k|v and gate|up, the 16-wave
+    two-tile kernel for down's long K slices at T = 8, one-tile o)."""
+    wl = synth.workload(4)
+    ow = OracleWorkload(wl, DEV, cache_w0=8)
+    announce("load workload 4 (8.7 GB arena)")
+    b = sdev.load(wl, DEV)
+    for T in (4, 8):
+        for call, _ in synth.CALLS:
+            x = wl.x(0, call, T, DEV)
+            announce(f"workload 4 layer 0 {call} T={T}")
+            y = run_call(b, 0, call, x)
+            torch.cuda.synchronize()
+            check(y, ow.call(0, call, np64(x)), f"w4 layer 0 {call} T={T}")
+    del b
+    torch.cuda.empty_cache()
+
+
 # --------------------------------------------------------------------------
 # workload 5: Gemma-4-31B mixed prefill, G=1 per type, r=1024, T=512
 # --------------------------------------------------------------------------
