@@ -146,7 +146,9 @@ __device__ __forceinline__ void kblock_fp8(f32x4 &acc, const uint8_t *arow, cons
 // 1-D grid: first the V^T tiles (full K, so z needs no summation later; they
 // are dispatched first and finish well inside the launch), then the W0 tiles,
 // each split into KS slices of K.
-template <int W, int UNROLL>
+// XL (FP8 W0 at T = 1): x staged in LDS (dynamic shared memory of
+// ceil(pairs / KS) * 128 bytes).
+template <int W, int UNROLL, bool XL = false>
 __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_part, uint16_t *z_pair, int ntile_vt,
                                                         int KS) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -182,7 +184,39 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
     const uint16_t *xrow8 = c.x + static_cast<size_t>(tok_ok ? r16 : 0) * K + g * 16;
     const int pfull_end = min(p_end, K >> 6);  // pairs entirely inside K
     const int npb = max(0, pfull_end - p_begin) / kFp8Unroll;
-    for (int b = wave; b < npb; b += W) kblock_fp8<kFp8Unroll>(acc, arow8, xrow8, tok_ok, p_begin + b * kFp8Unroll);
+    if constexpr (XL) {
+      // one token: the slice's x row staged in LDS once per workgroup, so
+      // the loop issues one global load (16 codes) per two MFMA steps rather
+      // than three
+      extern __shared__ u32x4 xs[];
+      const int nch = (p_end - p_begin) * 8;
+      for (int t = threadIdx.x; t < nch; t += W * 64) {
+        const int k = p_begin * 64 + t * 8;
+        xs[t] = k < K ? ld16(c.x + k) : zero4;
+      }
+      __syncthreads();
+      for (int b = wave; b < npb; b += W) {
+        const int p0 = p_begin + b * kFp8Unroll;
+        u32x4 av[kFp8Unroll], b0[kFp8Unroll], b1[kFp8Unroll];
+#pragma unroll
+        for (int j = 0; j < kFp8Unroll; ++j) av[j] = *reinterpret_cast<const u32x4 *>(arow8 + (p0 + j) * 64);
+#pragma unroll
+        for (int j = 0; j < kFp8Unroll; ++j) {
+          const int base = (p0 + j - p_begin) * 8 + g * 2;
+          b0[j] = tok_ok ? xs[base] : zero4;
+          b1[j] = tok_ok ? xs[base + 1] : zero4;
+        }
+#pragma unroll
+        for (int j = 0; j < kFp8Unroll; ++j) {
+          u32x4 lo, hi;
+          fp8x16_to_bf16(av[j], lo, hi);
+          acc = mfma16x16x32(lo, b0[j], acc);
+          acc = mfma16x16x32(hi, b1[j], acc);
+        }
+      }
+    } else {
+      for (int b = wave; b < npb; b += W) kblock_fp8<kFp8Unroll>(acc, arow8, xrow8, tok_ok, p_begin + b * kFp8Unroll);
+    }
     for (int pp = p_begin + npb * kFp8Unroll + wave; pp < p_end; pp += W) {
       const int k0 = pp * 64 + g * 16;
       const u32x4 a = k0 < c.ldw0 ? *reinterpret_cast<const u32x4 *>(arow8 + pp * 64) : zero4;
@@ -603,8 +637,15 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hip
   } else {
     KS = c.W0f8 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV) : decode_k_slices(c.Ntot, c.Rz, c.K);
     const int nt_vt = (c.Rz + 15) / 16;
-    hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nt_vt + nt_w0 * KS),
-                       dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
+    if (c.T == 1 && c.W0f8 != nullptr) {
+      const int npairs = (c.K + 63) / 64, pper = (npairs + KS - 1) / KS;
+      hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll, true>), dim3(nt_vt + nt_w0 * KS),
+                         dim3(kStreamWaves * 64), static_cast<size_t>(pper) * 128, stream, c, p_part, z_pair, nt_vt,
+                         KS);
+    } else {
+      hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nt_vt + nt_w0 * KS),
+                         dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
