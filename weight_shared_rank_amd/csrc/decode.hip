@@ -49,7 +49,7 @@ namespace {
 #define WL_STREAM_UNROLL 4
 #endif
 #ifndef WL_EPI_WAVES
-#define WL_EPI_WAVES 4
+#define WL_EPI_WAVES 2
 #endif
 #ifndef WL_DECODE_TARGET_WGS
 #define WL_DECODE_TARGET_WGS 4096
