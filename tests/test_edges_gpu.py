@@ -285,3 +285,31 @@ def test_long_k_slices_several_tokens(gpu_lib, T):
             torch.cuda.synchronize()
             res = compare(np64(y), ow.call(layer, c, np64(x)))
             assert res["ok"], f"layer {layer} {c} T={T}: {res}"
+
+
+@pytest.fixture(scope="module")
+def four_tile_bundle(gpu_lib):
+    # o: 1000 x 1064 (K slices of 5 k-steps, the last slice empty, a K tail);
+    # down: 33000 x 4104 (4 slices of 33 k-steps, a K tail); both row counts
+    # end in a partial 64-row group
+    dims = {(0, "o"): (1000, 1064), (0, "down"): (33000, 4104)}
+    wl = synth.custom(1, 1, 5, dims, cid=62)
+    return wl, OracleWorkload(wl, DEV), sdev.load(wl, DEV)
+
+
+@pytest.mark.parametrize("T", [8, 11, 16])
+def test_four_row_tiles_many_tokens(four_tile_bundle, T):
+    """From eight tokens on, calls whose several-token split stays within 8
+    K slices at four row tiles per workgroup run the four-tile stream kernel:
+    single k-steps for the short slices of o here, two-step blocks for the
+    long slices of down; against the oracle, and bitwise run to run."""
+    wl, ow, b = four_tile_bundle
+    for c in ("o", "down"):
+        x = wl.x(0, c, T, DEV)
+        announce(f"four row tiles T={T} {c}")
+        y = b.linear(0, c, x)
+        y2 = b.linear(0, c, x)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), c
+        res = compare(np64(y), ow.call(0, c, np64(x)))
+        assert res["ok"], f"{c} T={T}: {res}"

@@ -63,6 +63,9 @@ namespace {
 #ifndef WL_STREAM_WIDE_MIN_T
 #define WL_STREAM_WIDE_MIN_T 8
 #endif
+#ifndef WL_STREAM_ROWS4_MIN_T
+#define WL_STREAM_ROWS4_MIN_T 8
+#endif
 #ifndef WL_DECODE_TARGET_WGS_ROWS
 #define WL_DECODE_TARGET_WGS_ROWS 2048
 #endif
@@ -78,6 +81,8 @@ constexpr int kEpiWaves = WL_EPI_WAVES;
 constexpr int kStreamRows = WL_STREAM_ROWS;         // row tiles per stream workgroup for T >= kStreamRowsMinT
 constexpr int kStreamRowsMinT = WL_STREAM_ROWS_MIN_T;
 constexpr int kStreamWideMinT = WL_STREAM_WIDE_MIN_T;
+// from this many tokens on, W0 workgroups own twice kStreamRows row tiles
+constexpr int kStreamRows4MinT = WL_STREAM_ROWS4_MIN_T;
 constexpr int kTargetWgs = WL_DECODE_TARGET_WGS;
 // K slices of the several-token path come from a lower workgroup target:
 // each slice writes a T-token-wide fp32 partial that the epilogue re-reads
@@ -616,12 +621,28 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hip
   const int nt_w0 = (c.Ntot + 15) / 16;
   int KS;
   const int KS1 = decode_k_slices(c.Ntot, c.Rz, c.K);
-  constexpr int R = kStreamRows;
-  if (c.W0f8 == nullptr && c.T >= kStreamRowsMinT && KS1 * R <= kDecodeMaxSlices) {
+  constexpr int R = kStreamRows, R4 = 2 * kStreamRows;
+  const int ks_rows = min(KS1, k_slices_for(c.Ntot, c.Rz, c.K, kTargetWgsRows));
+  if (c.W0f8 == nullptr && c.T >= kStreamRows4MinT && R4 * ks_rows <= kDecodeMaxSlices) {
+    // eight or more tokens: R4 row tiles per W0 workgroup share each x
+    // fragment (the x bytes pulled from L2 per W0 byte halve again), with R4
+    // times the slices of the several-token target; blocks of two k-steps
+    // where every wave gets at least two such blocks of a slice, else single
+    // steps, so the slice's steps stay spread over all waves
+    KS = R4 * ks_rows;
+    const int per = ((c.K + 31) / 32 + KS - 1) / KS;
+    const int nw_w0 = (c.Ntot + 16 * R4 - 1) / (16 * R4), nt_vt = (c.Rz + 15) / 16;
+    if (per >= 2 * 2 * kStreamWaves)
+      hipLaunchKernelGGL((stream_rows_kernel<kStreamWaves, 2, R4>), dim3(nt_vt + nw_w0 * KS),
+                         dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
+    else
+      hipLaunchKernelGGL((stream_rows_kernel<kStreamWaves, 1, R4>), dim3(nt_vt + nw_w0 * KS),
+                         dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
+  } else if (c.W0f8 == nullptr && c.T >= kStreamRowsMinT && KS1 * R <= kDecodeMaxSlices) {
     // several tokens: R row tiles per W0 workgroup share each x fragment,
     // with R times the slices of the lower several-token target (never more
     // than the R * KS1 <= kDecodeMaxSlices checked above)
-    KS = R * min(KS1, k_slices_for(c.Ntot, c.Rz, c.K, kTargetWgsRows));
+    KS = R * ks_rows;
     const int nw_w0 = (c.Ntot + 16 * R - 1) / (16 * R), nt_vt = (c.Rz + 15) / 16;
     hipLaunchKernelGGL((stream_rows_kernel<kStreamWaves, kStreamUnroll, R>), dim3(nt_vt + nw_w0 * KS),
                        dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
