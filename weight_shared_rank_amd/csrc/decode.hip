@@ -69,6 +69,9 @@ namespace {
 #ifndef WL_DECODE_TARGET_WGS_ROWS
 #define WL_DECODE_TARGET_WGS_ROWS 2048
 #endif
+#ifndef WL_DECODE_TARGET_WGS_ROWS4
+#define WL_DECODE_TARGET_WGS_ROWS4 1024
+#endif
 #ifndef WL_FP8_UNROLL
 #define WL_FP8_UNROLL 2
 #endif
@@ -87,6 +90,9 @@ constexpr int kTargetWgs = WL_DECODE_TARGET_WGS;
 // K slices of the several-token path come from a lower workgroup target:
 // each slice writes a T-token-wide fp32 partial that the epilogue re-reads
 constexpr int kTargetWgsRows = WL_DECODE_TARGET_WGS_ROWS;
+// and the four-tile path's from a lower one still (the 31B q|k|v then runs 4
+// slices of 42 k-steps instead of 8 of 21)
+constexpr int kTargetWgsRows4 = WL_DECODE_TARGET_WGS_ROWS4;
 constexpr int kFp8Unroll = WL_FP8_UNROLL;
 
 // One batch of UNROLL complete k-steps (32 k each): loads first, then MFMAs.
@@ -623,13 +629,14 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hip
   const int KS1 = decode_k_slices(c.Ntot, c.Rz, c.K);
   constexpr int R = kStreamRows, R4 = 2 * kStreamRows;
   const int ks_rows = min(KS1, k_slices_for(c.Ntot, c.Rz, c.K, kTargetWgsRows));
-  if (c.W0f8 == nullptr && c.T >= kStreamRows4MinT && R4 * ks_rows <= kDecodeMaxSlices) {
+  const int ks_rows4 = min(KS1, k_slices_for(c.Ntot, c.Rz, c.K, kTargetWgsRows4));
+  if (c.W0f8 == nullptr && c.T >= kStreamRows4MinT && R4 * ks_rows4 <= kDecodeMaxSlices) {
     // eight or more tokens: R4 row tiles per W0 workgroup share each x
     // fragment (the x bytes pulled from L2 per W0 byte halve again), with R4
-    // times the slices of the several-token target; blocks of two k-steps
+    // times the slices of the four-tile target; blocks of two k-steps
     // where every wave gets at least two such blocks of a slice, else single
     // steps, so the slice's steps stay spread over all waves
-    KS = R4 * ks_rows;
+    KS = R4 * ks_rows4;
     const int per = ((c.K + 31) / 32 + KS - 1) / KS;
     const int nw_w0 = (c.Ntot + 16 * R4 - 1) / (16 * R4), nt_vt = (c.Rz + 15) / 16;
     if (per >= 2 * 2 * kStreamWaves)
