@@ -270,9 +270,9 @@ def test_outputs_with_two_byte_alignment(gpu_lib, T):
 @pytest.mark.parametrize("T", [7, 8, 13, 16])
 def test_long_k_slices_several_tokens(gpu_lib, T):
     """Calls whose K slices are long (K = 16392: 65 k-steps of 32 per slice at
-    8 slices; K = 8200: 33) with T >= 8 run the two-tile stream kernel with
-    twice the waves, in 4- and 2-step blocks; ragged rows (100 and 300:
-    partial 32-row pairs) and a K tail, against the oracle.  T = 7 takes the
+    8 slices; K = 8200: 33) with T >= 8 run the four-tile stream kernel with
+    twice the waves, in 2-step blocks; ragged rows (100 and 300: partial
+    64-row groups) and a K tail, against the oracle.  T = 7 takes the
     one-tile kernel."""
     dims = {(0, "o"): (300, 16392), (0, "down"): (100, 16392), (0, "q"): (300, 8200)}
     wl = synth.custom(2, 1, 5, dims, cid=61)

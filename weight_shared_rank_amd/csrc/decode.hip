@@ -655,19 +655,13 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hip
                        dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
   } else if (c.W0f8 == nullptr && c.T >= kStreamWideMinT && KS1 == kDecodeMaxSlices &&
              ((c.K + 31) / 32 + KS1 - 1) / KS1 >= 2 * kStreamWaves * 2) {
-    // several tokens, long K slices (o- and down-shaped calls): the two-tile
-    // kernel with twice the waves, so the workgroups halve but the waves in
-    // flight do not, at the full slice count; every wave still gets a block
-    // of k-steps (kStreamUnroll steps where the slice has enough, else 2)
+    // several tokens, long K slices (o- and down-shaped calls): R4 row tiles
+    // per workgroup on twice the waves at the full slice count, in 2-step
+    // blocks (every wave gets at least one)
     KS = KS1;
-    const int per = ((c.K + 31) / 32 + KS - 1) / KS;
-    const int nw_w0 = (c.Ntot + 16 * R - 1) / (16 * R), nt_vt = (c.Rz + 15) / 16;
-    if (per >= 2 * kStreamWaves * kStreamUnroll)
-      hipLaunchKernelGGL((stream_rows_kernel<2 * kStreamWaves, kStreamUnroll, R>), dim3(nt_vt + nw_w0 * KS),
-                         dim3(2 * kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
-    else
-      hipLaunchKernelGGL((stream_rows_kernel<2 * kStreamWaves, 2, R>), dim3(nt_vt + nw_w0 * KS),
-                         dim3(2 * kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
+    const int nw4 = (c.Ntot + 16 * R4 - 1) / (16 * R4), nt_vt = (c.Rz + 15) / 16;
+    hipLaunchKernelGGL((stream_rows_kernel<2 * kStreamWaves, 2, R4>), dim3(nt_vt + nw4 * KS),
+                       dim3(2 * kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
   } else {
     KS = c.W0f8 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV) : decode_k_slices(c.Ntot, c.Rz, c.K);
     const int nt_vt = (c.Rz + 15) / 16;
