@@ -23,6 +23,9 @@
 //     keeps ~16 significant bits and is the MFMA operand of launch 2.
 //     The V^T tiles are not split (z needs no summation) and come first in
 //     the grid, so they are dispatched early and end well inside the launch.
+//     With several tokens (bf16 W0) launch 1 is stream_rows_kernel instead:
+//     two or four 16-row tiles per workgroup share each x fragment, chosen
+//     by T and the call's slice lengths in launch_decode.
 //   launch 2 (epilogue_kernel): one workgroup per 16-row tile.  Its waves
 //     split the rank steps of U z: two MFMAs per 32 ranks (z_hi, then z_lo,
 //     as B operands) with U rows as the A operand; the waves' sums are reduced
