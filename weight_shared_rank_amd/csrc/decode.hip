@@ -410,8 +410,8 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
 
   // wave 0 loads the p partials and s of this lane's rows rbase..+3, token
   // r16; they are summed (in slice order) only after the delta, so these
-  // loads and those of U and z are in flight together.  Slices past KS and
-  // rows past Ntot re-read a valid address and are dropped.
+  // loads and those of U and z are in flight together.  Slices past KS are
+  // not loaded; rows past Ntot re-read a valid address and are dropped.
   f32x4 part[kDecodeMaxSlices];
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
   if (wave == 0 && tok_ok) {
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
         ((reinterpret_cast<uintptr_t>(c.s) | reinterpret_cast<uintptr_t>(qrow)) & 15) == 0) {
 #pragma unroll
       for (int s = 0; s < kDecodeMaxSlices; ++s)
-        part[s] = *reinterpret_cast<const f32x4 *>(pp + static_cast<size_t>(min(s, KS - 1)) * sstride + rbase);
+        part[s] = s < KS ? *reinterpret_cast<const f32x4 *>(pp + static_cast<size_t>(s) * sstride + rbase) : f32x4{0.f, 0.f, 0.f, 0.f};
       sc = *reinterpret_cast<const f32x4 *>(c.s + rbase);
       if (qrow) sc *= *reinterpret_cast<const f32x4 *>(qrow + rbase);
     } else {
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
       for (int i = 0; i < 4; ++i) {
         const int row = min(rbase + i, c.Ntot - 1);
 #pragma unroll
-        for (int s = 0; s < kDecodeMaxSlices; ++s) part[s][i] = pp[static_cast<size_t>(min(s, KS - 1)) * sstride + row];
+        for (int s = 0; s < kDecodeMaxSlices; ++s) part[s][i] = s < KS ? pp[static_cast<size_t>(s) * sstride + row] : 0.f;
         sc[i] = c.s[row] * (qrow ? qrow[row] : 1.f);
       }
     }
@@ -527,9 +527,9 @@ __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const
   const bool tok_ok = r16 < c.T;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  // wave 0: p partials and s of rows j0 + 4g + i of both halves (rows past
-  // N_g re-read row N_g - 1 of the half and are dropped); summed after the
-  // deltas so all loads are in flight together
+  // wave 0: p partials (slices < KS) and s of rows j0 + 4g + i of both halves
+  // (rows past N_g re-read row N_g - 1 of the half and are dropped); summed
+  // after the deltas so all loads are in flight together
   float part[2][kDecodeMaxSlices][4];
   float sc[2][4];
   if (wave == 0 && tok_ok) {
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const
         const int row = c.ch[hf].row_start + min(j0 + 4 * g + i, Ng - 1);
 #pragma unroll
         for (int s = 0; s < kDecodeMaxSlices; ++s)
-          part[hf][s][i] = pp[static_cast<size_t>(min(s, KS - 1)) * sstride + row];
+          part[hf][s][i] = s < KS ? pp[static_cast<size_t>(s) * sstride + row] : 0.f;
         sc[hf][i] = c.s[row] * (c.q ? c.q[row] : 1.f);
       }
   }
