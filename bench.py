@@ -36,6 +36,11 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 CALLS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
 
 
+def band_of_layer(layer, num_layers, num_bands):
+    from synth.device import band_of_layer as b
+    return b(layer, num_layers, num_bands)
+
+
 def log(msg):
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
@@ -104,7 +109,7 @@ class Step:
                 for f in fams_here:
                     if not wl.has(lt, f):
                         continue
-                    key = (wl.band(layer), 0 if f in ("gate", "up", "down") else lt, f)
+                    key = (band_of_layer(layer, wl.num_layers, wl.num_bands), 0 if f in ("gate", "up", "down") else lt, f)
                     if key in seen_w0:
                         N, K = wl.shape(lt, f)
                         self.bytes_band_unique -= N * K + 4 * N if w0_format == "fp8" else 2 * N * K
@@ -573,7 +578,7 @@ def band_reuse(dev, reps=5):
             tc, tr, tm, tp = (statistics.median(v) for v in (cold, reuse, model, repeat))
             between = sum(2 * wl.shape(0, f)[0] * wl.shape(0, f)[1] for c2, fs in calls if c2 != c for f in fs)
             out["cases"].append({
-                "workload": wl.name, "call": c, "layers": [layer, layer + 1], "same_band": wl.band(layer) == wl.band(layer + 1),
+                "workload": wl.name, "call": c, "layers": [layer, layer + 1], "same_band": band_of_layer(layer, wl.num_layers, wl.num_bands) == band_of_layer(layer + 1, wl.num_layers, wl.num_bands),
                 "w0_MB": w0 / 1e6, "bytes_read_MB": nbytes / 1e6, "other_w0_between_in_model_order_MB": between / 1e6,
                 "cold_us": tc * 1e6, "reuse_us": tr * 1e6, "model_order_us": tm * 1e6, "same_layer_repeat_us": tp * 1e6,
                 "cold_GBps": nbytes / tc / 1e9, "reuse_GBps": nbytes / tr / 1e9, "model_order_GBps": nbytes / tm / 1e9,

@@ -1,26 +1,49 @@
 """The oracle's view of a synthetic workload: fp64 bundle parameters and the
-expected output of each call.
+expected output of each call.  Test infrastructure: only the tests, the smoke
+check and the benchmark's CPU baseline use it; the HIP library never does.
 
-Directly drawn workloads take W0 per (band, layer type, family) -- MLP families
-share one block across layer types, as the mixed-attention adapter groups them
-("Decompose HF weights: the mixed-attention case") -- and s, U, V per layer.
-Decomposed workloads run ``decompose.decompose_band`` on the seeded per-layer
-weights of the band (and layer type) the layer belongs to.  With K=V tying,
-v has no bundle and its output is k's.
+Which bundle a call uses is decided here, from the workload's shape alone
+(its layer count, band count, layer types and K=V-tied types), never from the
+input generator:
+
+  * bands: layer l sits in band floor(l G / L) (``decompose.band_of``:
+    contiguous, balanced bands; "Quality (Gemma 4 31B)" page, "Decomposition
+    quality": 5 bands of 12 layers over 60);
+  * shared blocks: the attention families (q, k, v, o) keep one W0 per
+    (band, layer type, family); the MLP families (gate, up, down) keep one W0
+    per (band, family), shared by every layer type of the band ("Add a new
+    model architecture" page, "Decompose HF weights: the mixed-attention
+    case");
+  * K=V tying: on a tied layer type v has no bundle and its output is k's
+    output ("Decompose HF weights: the mixed-attention case",
+    attention_k_eq_v).
+
+Directly drawn workloads take W0 under that key from the generator and s, U, V
+per layer.  Decomposed workloads run ``decompose.decompose_band`` over the
+member layers of the W0 group (all layers of the band for an MLP family; the
+band's layers of one type for an attention family).
 """
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
 from . import forward, quant
-from .decompose import band_members, decompose_band
+from .decompose import band_of, decompose_band
 
+ATTENTION_FAMILIES = ("q", "k", "v", "o")
 _CALLS = {"qkv": ("q", "k", "v"), "o": ("o",), "gate_up": ("gate", "up"), "down": ("down",)}
 
 
 def to64(t):
     """Exact upcast of a bf16/fp32 torch tensor to a float64 numpy array."""
     return t.detach().to("cpu").float().double().numpy()
+
+
+def w0_key(band, ltype, fam):
+    """The W0 group of a family of a layer type in a band: (band, type key,
+    family), the type key being the layer type for attention families and 0
+    (one block for every type) for MLP families."""
+    return (band, ltype if fam in ATTENTION_FAMILIES else 0, fam)
 
 
 class OracleWorkload:
@@ -35,36 +58,50 @@ class OracleWorkload:
         self._cache_w0 = cache_w0
         self.w0_format = w0_format
 
+    # ---- resolution ------------------------------------------------------
+    def band(self, layer):
+        return band_of(layer, self.wl.num_layers, self.wl.num_bands)
+
+    def tied(self, layer, fam):
+        """v of a layer whose type ties v to k."""
+        return fam == "v" and self.wl.layer_types[layer] in self.wl.k_eq_v_types
+
+    def group_members(self, band, ltype, fam):
+        """Layers whose ``fam`` bundle uses the W0 of (band, ltype): those
+        with the same W0 key (every layer of the band for an MLP family, the
+        band's layers of type ltype for an attention family)."""
+        wl = self.wl
+        key = w0_key(band, ltype, fam)
+        return [l for l in range(wl.num_layers) if w0_key(self.band(l), wl.layer_types[l], fam) == key]
+
+    # ---- parameters ------------------------------------------------------
     def w0(self, band, ltype, fam):
-        key = (band, ltype if fam in ("q", "k", "v", "o") else 0, fam)
+        """Directly drawn workloads: the shared block of (band, ltype, fam)."""
+        key = w0_key(band, ltype, fam)
         if key not in self._w0:
             if len(self._w0) >= self._cache_w0:
                 self._w0.pop(next(iter(self._w0)))
-            w = to64(self.wl.w0(band, ltype, fam, self.device))
+            w = to64(self.wl.w0(key[0], key[1], fam, self.device))
             if self.w0_format == "fp8":
                 w = quant.dequantize(*quant.quantize_rows(w))
             self._w0[key] = w
         return self._w0[key]
+
+    def _decompose_group(self, key):
+        band, key_type, fam = key
+        members = self.group_members(band, key_type, fam)
+        Ws = [to64(self.wl.layer_weight(l, fam, self.device)) for l in members]
+        W0, res = decompose_band(Ws, self.wl.rank, store=True)
+        return W0, dict(zip(members, res))
 
     def prefetch_decompositions(self, keys, workers=8):
         """Decompose several (band, layer type, family) groups concurrently.
         Each decomposition is the same sequential computation as
         ``decomposed_band``; only the scheduling is parallel (LAPACK releases
         the GIL; each thread's BLAS is limited to one core)."""
-        todo = [k for k in keys if k not in self._dec]
+        todo = sorted({w0_key(*k) for k in keys} - set(self._dec))
         if not todo:
             return
-        wl = self.wl
-        inputs = {}
-        for (b, t, f) in todo:
-            members = [l for l in band_members(b, wl.num_layers, wl.num_bands) if wl.layer_types[l] == t]
-            inputs[(b, t, f)] = (members, [to64(wl.layer_weight(l, f, self.device)) for l in members])
-
-        def work(key):
-            members, Ws = inputs[key]
-            W0, res = decompose_band(Ws, wl.rank, store=True)
-            return key, (W0, dict(zip(members, res)))
-
         try:
             from threadpoolctl import threadpool_limits
             limiter = threadpool_limits(1)
@@ -72,50 +109,49 @@ class OracleWorkload:
             limiter = None
         try:
             with ThreadPoolExecutor(workers) as ex:
-                for key, val in ex.map(work, todo):
+                for key, val in zip(todo, ex.map(self._decompose_group, todo)):
                     self._dec[key] = val
         finally:
             if limiter is not None:
                 limiter.restore_original_limits()
 
-    def _tied(self, layer, fam):
-        return fam == "v" and self.wl.layer_types[layer] in self.wl.k_eq_v_types
-
     def decomposed_band(self, band, ltype, fam):
-        key = (band, ltype, fam)
+        """Decomposed workloads: (W0, {layer: {"s", "U", "V", ...}}) of the W0
+        group that (band, ltype, fam) belongs to."""
+        key = w0_key(band, ltype, fam)
         if key not in self._dec:
-            wl = self.wl
-            members = [l for l in band_members(band, wl.num_layers, wl.num_bands)
-                       if wl.layer_types[l] == ltype]
-            Ws = [to64(wl.layer_weight(l, fam, self.device)) for l in members]
-            W0, res = decompose_band(Ws, wl.rank, store=True)
-            self._dec[key] = (W0, dict(zip(members, res)))
+            self._dec[key] = self._decompose_group(key)
         return self._dec[key]
 
     def params(self, layer, fam):
-        """(W0, s, U, V) as fp64 arrays for one layer and family."""
+        """(W0, s, U, V) as fp64 arrays for one layer and family (k's bundle
+        for v on a tied layer type)."""
         wl = self.wl
-        if self._tied(layer, fam):
+        if self.tied(layer, fam):
             fam = "k"
         lt = wl.layer_types[layer]
+        band = self.band(layer)
         if wl.decomposed:
-            W0, per = self.decomposed_band(wl.band(layer), lt, fam)
+            W0, per = self.decomposed_band(band, lt, fam)
             m = per[layer]
             return W0, m["s"], m["U"], m["V"]
-        return (self.w0(wl.band(layer), lt, fam), to64(wl.s(layer, fam, self.device)),
+        return (self.w0(band, lt, fam), to64(wl.s(layer, fam, self.device)),
                 to64(wl.u(layer, fam, self.device)), to64(wl.v(layer, fam, self.device)))
 
     def families_of(self, layer, call):
+        """The families a call evaluates on this layer, in output order (a
+        tied v stays: its slot repeats k)."""
         fams = _CALLS.get(call, (call,))
         lt = self.wl.layer_types[layer]
-        return [f for f in fams if (lt, f) in self.wl.dims or self._tied(layer, f)]
+        return [f for f in fams if (lt, f) in self.wl.dims or self.tied(layer, f)]
 
     def call(self, layer, call, x):
         """Expected fp64 output of a single-family or stacked call."""
         x = np.asarray(x, np.float64)
-        children = []
-        for f in self.families_of(layer, call):
-            children.append("dup" if self._tied(layer, f) else self.params(layer, f))
+        fams = self.families_of(layer, call)
+        if len(fams) == 1:
+            return forward.factored(x, *self.params(layer, fams[0]))
+        children = ["dup" if self.tied(layer, f) else self.params(layer, f) for f in fams]
         return forward.stacked(x, children)
 
     def gate_up_act(self, layer, x, name):

@@ -102,13 +102,13 @@ class Workload:
         return min(self.rank, n, k)
 
     # ---- tensors -------------------------------------------------------
-    def w0(self, band: int, ltype: int, fam: str, device="cpu") -> torch.Tensor:
-        """Directly drawn shared block, N(0, 1/in) in bf16.  Attention
-        families are keyed per layer type; MLP families share one block
-        across types (the mixed-attention adapter keeps MLP W0 per band)."""
-        n, k = self.shape(ltype, fam)
-        key_type = ltype if fam in ATTN_FAMILIES else 0
-        return _normal((n, k), _seed(self.root, "w0", band, key_type, FAM_ID[fam]),
+    def w0(self, index: int, key_type: int, fam: str, device="cpu") -> torch.Tensor:
+        """A directly drawn shared block, N(0, 1/in) in bf16, with the shape
+        of ``fam`` on layer type ``key_type``; its stream is keyed by
+        (index, key_type, family) exactly as given.  Which blocks a bundle
+        holds, and which layers use each, is the caller's business."""
+        n, k = self.shape(key_type, fam)
+        return _normal((n, k), _seed(self.root, "w0", index, key_type, FAM_ID[fam]),
                        0.0, 1.0 / math.sqrt(k), device).to(torch.bfloat16)
 
     def s(self, layer: int, fam: str, device="cpu") -> torch.Tensor:
@@ -144,10 +144,6 @@ class Workload:
         call_id = [c for c, _ in CALLS].index(call) if call in dict(CALLS) else 10 + FAM_ID[call]
         return _normal((T, k), _seed(self.root, "x", layer, call_id, T, salt), 0.0,
                        self.x_std, device).to(torch.bfloat16)
-
-    def band(self, layer: int) -> int:
-        """Contiguous balanced bands: layer l sits in band floor(l*G/L)."""
-        return (layer * self.num_bands) // self.num_layers
 
 
 def _gemma3_dims():

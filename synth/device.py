@@ -11,6 +11,12 @@ from typing import Callable, Optional
 from weight_shared_rank_amd import binding
 
 
+def band_of_layer(layer: int, num_layers: int, num_bands: int) -> int:
+    """The library's band of a layer, floor(l G / L) (the rule its header
+    states), used here only to list the W0 sources a bundle must be given."""
+    return (layer * num_bands) // num_layers
+
+
 def spec_of(wl, w0_format="bf16") -> binding.WlBundleSpec:
     ranks = {key: min(wl.rank, *wl.dims[key]) for key in wl.dims}
     return binding.make_spec(wl.num_layers, wl.num_bands, dict(wl.dims), ranks,
@@ -29,7 +35,7 @@ def sources_of(wl, device="cuda", tensors: Optional[Callable] = None, layers=Non
     srcs = []
     for b in range(wl.num_bands):
         for t in range(wl.num_layer_types):
-            members = [l for l in range(wl.num_layers) if wl.band(l) == b]
+            members = [l for l in range(wl.num_layers) if band_of_layer(l, wl.num_layers, wl.num_bands) == b]
             for fam in wl.families(t):
                 if not wl.has(t, fam):
                     continue

@@ -131,3 +131,50 @@ def test_activation_mutants_are_caught(monkeypatch, mutant):
         except AssertionError:
             caught += 1
     assert caught >= 1, f"{mutant.__name__} passed every activation pin"
+
+
+# --------------------------------------------------------------------------
+# call resolution (oracle.workload): band, shared-block group, tied child
+# --------------------------------------------------------------------------
+import test_oracle_resolution as res_pins  # noqa: E402
+from oracle import workload as owl  # noqa: E402
+
+
+def _interleaved(layer, L, G):
+    return layer % G
+
+
+def _per_type_mlp_key(band, ltype, fam):
+    return (band, ltype, fam)
+
+
+_orig_families_of = owl.OracleWorkload.families_of
+
+
+def _drop_tied_v(self, layer, call):
+    return [f for f in _orig_families_of(self, layer, call) if not self.tied(layer, f)]
+
+
+def _untied(self, layer, fam):
+    return False
+
+
+@pytest.mark.parametrize("name,target,attr,mutant", [
+    ("interleaved bands", owl, "band_of", _interleaved),
+    ("MLP W0 per layer type", owl, "w0_key", _per_type_mlp_key),
+    ("tied v dropped", owl.OracleWorkload, "families_of", _drop_tied_v),
+    ("v evaluated from its own bundle on tied types", owl.OracleWorkload, "tied", _untied),
+])
+def test_resolution_mutants_are_caught(monkeypatch, name, target, attr, mutant):
+    monkeypatch.setattr(target, attr, mutant)
+    caught = 0
+    for pin, args in [(res_pins.test_direct_workload_calls_match_hand_tables, ()),
+                      (res_pins.test_direct_workload_shares_mlp_blocks_across_types, ()),
+                      (res_pins.test_decomposed_blocks_are_group_means, ("gate",)),
+                      (res_pins.test_decomposed_blocks_are_group_means, ("q",)),
+                      (res_pins.test_band_table_is_contiguous, ())]:
+        try:
+            pin(*args)
+        except (AssertionError, KeyError, ValueError):
+            caught += 1
+    assert caught >= 1, f"{name} passed every resolution pin"

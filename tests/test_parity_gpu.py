@@ -52,7 +52,7 @@ def decoded_tensors(ow):
         wl = ow.wl
         if kind == "w0":
             return torch.from_numpy(ow.decomposed_band(index, ltype, fam)[0]).to(torch.bfloat16)
-        W0, per = ow.decomposed_band(wl.band(index), ltype, fam)
+        W0, per = ow.decomposed_band(ow.band(index), ltype, fam)
         m = per[index]
         if kind == "s":
             return torch.from_numpy(m["s"]).to(torch.float32)
@@ -99,7 +99,7 @@ def _decomposed_bundle(variant):
     wl = synth.workload(2, variant)
     ow = OracleWorkload(wl, DEV)
     announce(f"decompose workload 2 ({variant or 'G13'}) on the host")
-    ow.prefetch_decompositions([(wl.band(l), 0, f) for l in range(wl.num_layers) for f in synth.FAMILIES],
+    ow.prefetch_decompositions([(ow.band(l), 0, f) for l in range(wl.num_layers) for f in synth.FAMILIES],
                                workers=16)
     announce("load workload 2")
     return wl, sdev.load(wl, DEV, tensors=decoded_tensors(ow)), ow

@@ -43,4 +43,5 @@ def test_gemma_workloads():
     assert not w5.has(1, "v") and w5.shape(1, "v") == (8192, 5376)
     assert w5.shape(1, "q") == (16384, 5376) and w5.shape(0, "q") == (8192, 5376)
     w4 = synth.workload(4)
-    assert [w4.band(l) for l in (0, 11, 12, 59)] == [0, 0, 1, 4]
+    import synth.device as sdev
+    assert [sdev.band_of_layer(l, w4.num_layers, w4.num_bands) for l in (0, 11, 12, 59)] == [0, 0, 1, 4]
