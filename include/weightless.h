@@ -131,15 +131,24 @@ size_t theta_bundle_arena_bytes(const wl_bundle_spec *spec);
 
 /* Pack a theta bundle into the caller's device arena (d_arena, 256-byte
  * aligned, at least theta_bundle_arena_bytes(spec) bytes) on `stream`.
+ * The ownership follows the pages' model: each shared block W0 is declared
+ * once at model level and injected into every layer of its band ("Add a new
+ * model architecture" page, "Swap in the weightless layers"), and the layers
+ * hold only their s, U and V; pre-decomposed bundles are loaded as they are
+ * ("Decompose HF weights: the uniform case", the theta-dict passthrough).
  * Every source the spec implies must appear exactly once in srcs[0..n_src);
  * any other source is an error.  The library never decomposes: sources are
- * already-decomposed bundles.  Device sources may be reused or freed once the
- * stream has passed this point; host sources as soon as the call returns.
+ * already-decomposed bundles.  Nothing is synchronized: device sources may be
+ * reused or freed once the stream has passed this point, host sources as soon
+ * as the call returns (host V sources are transposed into host buffers owned
+ * by the handle, so the handle must not be freed before the stream has passed
+ * the load).
  * On success *out receives a handle that refers to the arena (not owning it). */
 wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size_t n_src,
                             void *d_arena, size_t arena_bytes, void *stream, wl_bundle **out);
 
-/* Free the host handle (never the arena).  NULL is accepted. */
+/* Free the host handle (never the arena).  NULL is accepted.  Call it only
+ * after the stream of its theta_bundle_load has passed the load. */
 wl_status theta_bundle_free(wl_bundle *bundle);
 
 /* Workspace bytes needed by any weightless_linear / weightless_stacked_linear
@@ -150,7 +159,11 @@ wl_status theta_bundle_free(wl_bundle *bundle);
  * 0 with wl_last_error() set on error. */
 size_t weightless_workspace_bytes(const wl_bundle *bundle, int32_t T);
 
-/* y = s (.) (W0 x) + U (V^T x) for one family of one layer.
+/* y = s (.) (W0 x) + U (V^T x) for one family of one layer: the forward of
+ * a weightless projection ("Add a new model architecture" page,
+ * introduction: shared block, per-row scale and low-rank delta in place of
+ * the dense weight; "Quality (Gemma 4 31B)" page, "Kernel optimizations >
+ * GEMM path": bf16 operands, fp32 accumulation).
  *  d_x bf16 [T, K], d_y bf16 [T, N] (must not alias d_x), T >= 0 (T = 0: no-op).
  *  T <= 16 runs the decode path (two launches: one streams [W0; V^T] x into
  *  fp32 K-slice partials of W0 x and z = V^T x, the other sums them, scales
@@ -164,7 +177,10 @@ wl_status weightless_linear(const wl_bundle *bundle, int32_t layer, int32_t fami
                             const void *d_x, int32_t T, void *d_y,
                             void *d_ws, size_t ws_bytes, void *stream);
 
-/* The stacked call: q|k|v (or gate|up) of one layer over one x: the same
+/* The stacked call ("Quality (Gemma 4 31B)" page, "Kernel optimizations >
+ * GEMM path": the q, k and v projections of a layer batched into one call
+ * over their shared input; K=V tying from "Decompose HF weights: the
+ * mixed-attention case"): q|k|v (or gate|up) of one layer over one x: the same
  * launches as a single-family call, over all children's rows at once.  d_y bf16 [T, N_q + N_k + N_v] (resp.
  * [T, N_gate + N_up]).  On a K=V-tied layer type the v slot receives a copy of
  * k's output, so the output layout is the same on every layer. */

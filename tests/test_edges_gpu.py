@@ -236,6 +236,25 @@ def test_split_k_prefill(gpu_lib, T):
             assert res["ok"], f"layer {layer} {c}: {res}"
 
 
+@pytest.mark.parametrize("T", [40, 200])
+def test_split_k_finish_with_unaligned_scale(gpu_lib, T):
+    """A single-family call's s is a row slice of its group's s: after a q of
+    4098 rows, k's s starts 8 bytes past a 16-byte boundary.  k (520 rows, a
+    multiple of 4, long K) takes the split-K finish path, which must not use
+    16-byte loads of s there."""
+    dims = {(0, "q"): (4098, 4096), (0, "k"): (520, 4096), (0, "v"): (520, 4096)}
+    wl = synth.custom(1, 1, 32, dims, cid=78)
+    ow = OracleWorkload(wl, DEV)
+    b = sdev.load(wl, DEV)
+    for c in ("k", "v", "qkv"):
+        x = wl.x(0, c, T, DEV)
+        announce(f"split-K finish, unaligned s, T={T} {c}")
+        y = call(b, 0, c, x)
+        torch.cuda.synchronize()
+        res = compare(np64(y), ow.call(0, c, np64(x)))
+        assert res["ok"], f"{c}: {res}"
+
+
 @pytest.mark.parametrize("T", [1, 16, 40, 130])
 def test_outputs_with_two_byte_alignment(gpu_lib, T):
     """y (and the fused gate|up h) need only 2-byte alignment: outputs written

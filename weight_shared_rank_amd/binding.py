@@ -171,10 +171,15 @@ class ThetaBundle:
                                        self.arena.numel(), _stream_ptr(stream), ctypes.byref(h)))
         self.handle = h
         self._keep_until_sync = keep
+        # the load is asynchronous: the handle (which owns the host-side V^T
+        # copies) is freed only once the stream has passed this event
+        self._loaded = torch.cuda.Event()
+        self._loaded.record(stream if stream is not None else torch.cuda.current_stream())
         self._ws = {}
 
     def close(self):
         if getattr(self, "handle", None):
+            self._loaded.synchronize()
             lib().theta_bundle_free(self.handle)
             self.handle = None
 

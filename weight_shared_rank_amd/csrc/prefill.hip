@@ -636,7 +636,9 @@ __global__ void finish_kernel(FinishArgs a) {
   const size_t plane = static_cast<size_t>(a.T) * a.M;
   const float *p = a.P + static_cast<size_t>(tok) * a.M + row;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
-  if (row + 3 < a.M && (a.M & 3) == 0) {
+  // the 16-byte loads need s 16-byte aligned too: a single-family call's s
+  // is a row slice of its group's s (q with a ragged N shifts k's)
+  if (row + 3 < a.M && (a.M & 3) == 0 && (reinterpret_cast<uintptr_t>(a.s) & 15) == 0) {
     if (a.has_delta) d = *reinterpret_cast<const f32x4 *>(p + a.ksplit * plane);
     sc = *reinterpret_cast<const f32x4 *>(a.s + row);
     // four slices' loads in flight at a time (slices past the last re-read

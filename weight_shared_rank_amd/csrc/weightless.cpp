@@ -31,6 +31,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -294,6 +295,9 @@ struct wl_bundle {
   Layout lo;
   uint8_t *arena = nullptr;
   size_t arena_bytes = 0;
+  // V^T of host-resident V sources, transposed on the host; the load's
+  // copies read them on the stream, so they live as long as the handle
+  std::vector<std::vector<uint16_t>> host_vt;
 };
 
 namespace {
@@ -519,12 +523,10 @@ wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size
   uint8_t *A = static_cast<uint8_t *>(d_arena);
   hipError_t e = wl::launch_fill_zero(A, lo.bytes, strm);
   if (e != hipSuccess) return hip_fail(e, "arena fill");
-  std::vector<std::vector<uint16_t>> host_tmp;
-  bool any_host = false;
+  std::unique_ptr<wl_bundle> h(new wl_bundle);
   for (const auto &kv : expect) {
     const wl_src &s = srcs[kv.second];
     const hipMemcpyKind kind = s.on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
-    any_host |= !s.on_device;
     if (s.kind == WL_SRC_W0) {
       const int t = kv.first[2];
       const int g = kGroupOf[s.family];
@@ -563,8 +565,8 @@ wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size
         e = wl::launch_transpose_v(static_cast<const uint16_t *>(s.ptr), K, r, dst, strm);
       } else {
         const uint16_t *V = static_cast<const uint16_t *>(s.ptr);
-        host_tmp.emplace_back(static_cast<size_t>(r) * K);
-        std::vector<uint16_t> &vt = host_tmp.back();
+        h->host_vt.emplace_back(static_cast<size_t>(r) * K);
+        std::vector<uint16_t> &vt = h->host_vt.back();
         for (int k = 0; k < K; ++k)
           for (int j = 0; j < r; ++j) vt[static_cast<size_t>(j) * K + k] = V[static_cast<size_t>(k) * r + j];
         e = hipMemcpyAsync(dst, vt.data(), vt.size() * 2, hipMemcpyHostToDevice, strm);
@@ -572,15 +574,10 @@ wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size
     }
     if (e != hipSuccess) return hip_fail(e, "bundle copy");
   }
-  if (any_host) {
-    e = hipStreamSynchronize(strm);
-    if (e != hipSuccess) return hip_fail(e, "stream synchronize after host copies");
-  }
-  wl_bundle *h = new wl_bundle;
   h->lo = std::move(lo);
   h->arena = A;
   h->arena_bytes = arena_bytes;
-  *out = h;
+  *out = h.release();
   g_err.clear();
   return WL_OK;
 }
