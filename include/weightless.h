@@ -177,6 +177,25 @@ wl_status weightless_linear(const wl_bundle *bundle, int32_t layer, int32_t fami
                             const void *d_x, int32_t T, void *d_y,
                             void *d_ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * call as weightless_linear (same launches and results), with its workspace
+ * taken from a fixed array of WL_NOALLOC_WORKSPACE_BYTES bytes of device
+ * memory inside the library instead of a caller buffer.  Each GPU holds its
+ * own array, reserved when the library is first used on that GPU and kept
+ * until the process ends; its address is looked up once per device, on the
+ * current device (the stream must belong to it).  Calls that need more
+ * workspace than the array holds (weightless_workspace_bytes(bundle, T) >
+ * WL_NOALLOC_WORKSPACE_BYTES, e.g. long prefill calls of big bundles or
+ * prefill on an FP8 bundle) return WL_ENOSPACE before enqueuing anything.
+ * Nothing is allocated and the array needs no initialization, but every call
+ * on one GPU shares it: calls that may overlap on one GPU (on different
+ * streams, or from several threads without ordering) race and must be
+ * serialized by the caller. */
+#define WL_NOALLOC_WORKSPACE_BYTES (64u << 20)
+wl_status weightless_linear_noalloc(const wl_bundle *bundle, int32_t layer, int32_t family, const void *d_x,
+                                    int32_t T, void *d_y, void *stream);
+
 /* The stacked call ("Quality (Gemma 4 31B)" page, "Kernel optimizations >
  * GEMM path": the q, k and v projections of a layer batched into one call
  * over their shared input; K=V tying from "Decompose HF weights: the

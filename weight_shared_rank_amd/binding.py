@@ -26,11 +26,12 @@ STATUS = {0: "WL_OK", -1: "WL_EINVAL", -2: "WL_ESHAPE", -3: "WL_EDTYPE", -4: "WL
           -5: "WL_ENOSPACE", -6: "WL_EHIP"}
 MAX_TYPES = 2
 DECODE_MAX_T = 16
+NOALLOC_WORKSPACE_BYTES = 64 << 20    # WL_NOALLOC_WORKSPACE_BYTES
 
 # every symbol include/weightless.h declares
 EXPORTS = ("theta_bundle_arena_bytes", "theta_bundle_load", "theta_bundle_free",
            "weightless_workspace_bytes",
-           "weightless_linear", "weightless_stacked_linear", "weightless_out_dim", "wl_last_error",
+           "weightless_linear", "weightless_linear_noalloc", "weightless_stacked_linear", "weightless_out_dim", "wl_last_error",
            "weightless_materialize_workspace_bytes", "weightless_materialize", "weightless_gate_up_act",
            "weightless_decompose_workspace_bytes", "weightless_decompose")
 
@@ -74,6 +75,7 @@ def lib():
         "theta_bundle_free": (i32, [vp]),
         "weightless_workspace_bytes": (sz, [vp, i32]),
         "weightless_linear": (i32, [vp, i32, i32, vp, i32, vp, vp, sz, vp]),
+        "weightless_linear_noalloc": (i32, [vp, i32, i32, vp, i32, vp, vp]),
         "weightless_stacked_linear": (i32, [vp, i32, i32, vp, i32, vp, vp, sz, vp]),
         "weightless_out_dim": (i32, [vp, i32, i32, i32]),
         "wl_last_error": (ctypes.c_char_p, []),
@@ -231,6 +233,17 @@ class ThetaBundle:
         """y = s*(W0 x) + U (V^T x) for one family; x bf16 [T, K] on the device."""
         return self._call(lib().weightless_linear, layer, FAMILY[family], x, y, ws, stream,
                           self.out_dim(layer, family=family))
+
+    def linear_noalloc(self, layer: int, family: str, x, y=None, stream=None):
+        """weightless_linear on the library's fixed device workspace (no
+        caller workspace); y is allocated here only if not given."""
+        import torch
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.out_dim(layer, family=family)), dtype=torch.bfloat16, device=x.device)
+        _check(lib().weightless_linear_noalloc(self.handle, layer, FAMILY[family], x.data_ptr(), T, y.data_ptr(),
+                                               _stream_ptr(stream)))
+        return y
 
     def stacked(self, layer: int, stack: str, x, y=None, ws=None, stream=None):
         """The stacked q|k|v or gate|up call over one x."""

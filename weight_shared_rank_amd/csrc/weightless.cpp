@@ -32,6 +32,7 @@
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -442,6 +443,34 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
   return WL_OK;
 }
 
+// Fixed device workspace of weightless_linear_noalloc, for callers that
+// cannot allocate.  Each device holds its own copy of the array for the life
+// of the process; host code uses only the address hipGetSymbolAddress returns
+// for the current device (the array's name is a host-side stand-in).
+__device__ __align__(256) uint8_t scratch[WL_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch array, looked up once per device.
+wl_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(WL_EINVAL, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(WL_EHIP, "hipGetSymbolAddress(scratch) returned NULL on device %d", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WL_OK;
+}
+
 }  // namespace
 
 namespace wl {
@@ -602,6 +631,22 @@ size_t weightless_workspace_bytes(const wl_bundle *bundle, int32_t T) {
 wl_status weightless_linear(const wl_bundle *bundle, int32_t layer, int32_t family, const void *d_x, int32_t T,
                             void *d_y, void *d_ws, size_t ws_bytes, void *stream) {
   return run_call(bundle, layer, family, -1, d_x, T, d_y, d_ws, ws_bytes, stream);
+}
+
+wl_status weightless_linear_noalloc(const wl_bundle *bundle, int32_t layer, int32_t family, const void *d_x,
+                                    int32_t T, void *d_y, void *stream) {
+  if (!bundle) return fail(WL_EINVAL, "bundle is NULL");
+  if (T < 0) return fail(WL_EINVAL, "T = %d is negative", T);
+  if (T > kMaxDim) return fail(WL_ESHAPE, "T = %d too large", T);
+  const size_t need = ws_bytes_for(bundle->lo, T);
+  if (need > WL_NOALLOC_WORKSPACE_BYTES)
+    return fail(WL_ENOSPACE, "this call needs %zu bytes of workspace; the fixed workspace of "
+                "weightless_linear_noalloc holds %zu (use weightless_linear with a caller workspace)",
+                need, static_cast<size_t>(WL_NOALLOC_WORKSPACE_BYTES));
+  void *ws = nullptr;
+  const wl_status st = scratch_of_current_device(&ws);
+  if (st != WL_OK) return st;
+  return run_call(bundle, layer, family, -1, d_x, T, d_y, ws, WL_NOALLOC_WORKSPACE_BYTES, stream);
 }
 
 wl_status weightless_stacked_linear(const wl_bundle *bundle, int32_t layer, int32_t stack, const void *d_x, int32_t T,
