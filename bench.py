@@ -410,6 +410,251 @@ def cpu_baseline(wl, T, budget_s, dev):
                       f"of bundle bytes), repeated {n}x in {el:.1f} s; W0/s/U/V pre-upcast to fp64 outside the timing"}
 
 
+def _host_info():
+    """Threads the host BLAS uses and its name."""
+    cores, blas = os.cpu_count(), "unknown BLAS"
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        libs = [i for i in info if i.get("user_api") == "blas"]
+        if libs:
+            cores = libs[0].get("num_threads", cores)
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    return cores, blas
+
+
+def _oracle_children(ow, wl, layer, fams):
+    """fp64 parameters of a call's children (k's bundle again for a tied v),
+    upcast outside any timing."""
+    out = []
+    for f in fams:
+        if ow.tied(layer, f):
+            out.append("dup")
+        elif (wl.layer_types[layer], f) in wl.dims:
+            out.append(ow.params(layer, f))
+    return out
+
+
+def oracle_calls_timing(wl, T, layers, calls, dev, repeats=1, budget_s=None):
+    """The fp64 oracle (as it stands: oracle.forward on numpy's BLAS) on
+    every call of the given layers.  Each call is timed `repeats` times and
+    its median kept (or, with budget_s, the layers' calls are repeated until
+    about budget_s has passed).  Returns seconds per pass over the calls,
+    algorithmic bytes and flops of one pass, and the pass count."""
+    import statistics
+    import numpy as np
+    from oracle import forward
+    from oracle.workload import OracleWorkload
+    ow = OracleWorkload(wl, dev, cache_w0=16)
+    prepared = []
+    nbytes = nflops = 0
+    for layer in layers:
+        for name, fams in calls:
+            fams_here = [f for f in fams if (wl.layer_types[layer], f) in wl.dims or ow.tied(layer, f)]
+            x = wl.x(layer, name, T, dev).float().cpu().double().numpy()
+            prepared.append((x, _oracle_children(ow, wl, layer, fams_here)))
+            nbytes += call_bytes(wl, layer, fams_here, T)[0]
+            nflops += call_flops(wl, layer, fams_here, T)
+    del ow
+
+    def one(x, ch):
+        return forward.stacked(x, ch) if len(ch) > 1 else forward.factored(x, *ch[0])
+    if budget_s is not None:
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            for x, ch in prepared:
+                one(x, ch)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or n >= 5000:
+                break
+        return el / n, nbytes, nflops, n
+    per_call = []
+    for x, ch in prepared:
+        ts = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            one(x, ch)
+            ts.append(time.perf_counter() - t0)
+        per_call.append(statistics.median(ts))
+    return sum(per_call), nbytes, nflops, repeats
+
+
+def oracle_prefill_baselines(dev):
+    """The fp64 oracle beside the prefill figures: the Gemma-4-31B mixed
+    prefill (T=512) on one sliding and one full-attention layer, every call
+    once; the Gemma-3-1B prefill (T=2048) on one layer's seven single-family
+    calls, median of 3."""
+    import synth
+    cores, blas = _host_info()
+    w5 = synth.workload(5)
+    full = w5.layer_types.index(1)
+    t5, _, f5, _ = oracle_calls_timing(w5, 512, [0, full], CALLS, dev, repeats=1)
+    singles = tuple((f, (f,)) for f in synth.FAMILIES)
+    t3, _, f3, _ = oracle_calls_timing(synth.workload(3), 2048, [0], singles, dev, repeats=3)
+    return {"value": f5 / t5 / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle ({blas}) on the gemma4-31b mixed prefill at T=512: layer 0 (sliding) and "
+                      f"layer {full} (full attention), each call once: {f5 / 1e12:.3f} TFLOP in {t5:.2f} s; "
+                      f"parameters pre-upcast to fp64 outside the timing",
+            "gemma3_1b_T2048": {"value": f3 / t3 / 1e12, "unit": "TFLOP/s",
+                                "sample": f"layer 0, 7 single-family calls, median of 3 per call: "
+                                          f"{f3 / 1e9:.1f} GFLOP in {t3:.3f} s"}}
+
+
+def oracle_small_decode_baselines(dev, budget_s=2.0):
+    """The fp64 oracle on the two small decode workloads: the one-family
+    workload (both layers' calls, T=4, median of 3) and the Gemma-3-1B
+    shapes at T=1 (one layer's four calls, repeated for about budget_s)."""
+    import synth
+    cores, blas = _host_info()
+    w1 = synth.workload(1)
+    t1, b1, _, _ = oracle_calls_timing(w1, 4, [0, 1], (("up", ("up",)),), dev, repeats=3)
+    w2 = synth.custom(26, 13, 32, dict(synth.workload(2).dims), cid=2)
+    t2, b2, _, n2 = oracle_calls_timing(w2, 1, [0], CALLS, dev, budget_s=budget_s)
+    return {"cores": cores, "blas": blas,
+            "one_family_T4": {"GBps": b1 / t1 / 1e9, "us_per_call": t1 / 2 * 1e6,
+                              "sample": "both layers' up calls, median of 3 each"},
+            "gemma3_1b_T1": {"GBps": b2 / t2 / 1e9, "us_per_layer": t2 * 1e6,
+                             "sample": f"layer 0's four calls repeated {n2}x"}}
+
+
+def workload1_section(dev, steps, warmup, copies=64):
+    """The one-family workload (W0 4096 x 1152 shared by 2 layers, r=4, T=4)
+    as back-to-back graph-replayed calls, layer 0 then layer 1 (the second
+    re-reads the first's W0).  cold: the calls rotate through `copies`
+    bundle copies (distinct arenas, a working set of copies x 9.6 MB, over
+    twice the 256 MB Infinity Cache), so each pair starts from HBM; warm:
+    every pair on one bundle."""
+    import torch
+    import synth
+    import synth.device as sdev
+    wl = synth.workload(1)
+    bundles = [sdev.load(wl, dev) for _ in range(copies)]
+    xs = [wl.x(l, "up", 4, dev) for l in (0, 1)]
+    y = torch.empty((4, 4096), dtype=torch.bfloat16, device=dev)
+    ws = bundles[0].workspace(4)
+    nbytes = sum(call_bytes(wl, l, ["up"], 4)[0] for l in (0, 1))
+
+    class _Run:
+        def __init__(self, bs):
+            self.bs = bs
+
+        def run(self):
+            for b in self.bs:
+                for l in (0, 1):
+                    b.linear(l, "up", xs[l], y=y, ws=ws)
+    t_cold, g = time_graph(_Run(bundles), steps, warmup)
+    del g
+    t_warm, g = time_graph(_Run([bundles[0]] * copies), steps, warmup)
+    del g, bundles
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    calls = 2 * copies
+    return {"calls_per_replay": calls, "copies": copies, "bytes_per_call": nbytes / 2,
+            "cold_us_per_call": t_cold / calls * 1e6, "cold_GBps": nbytes * copies / t_cold / 1e9,
+            "warm_us_per_call": t_warm / calls * 1e6, "warm_GBps": nbytes * copies / t_warm / 1e9}
+
+
+def band_reuse_ab(dev, steps, warmup):
+    """Band reuse of W0, as an A/B of graph-replayed decode steps (T=1) with
+    the same kernels, launches and bytes, where only the W0 addresses
+    differ: a bundle whose consecutive layers share W0 (a band) against one
+    with a distinct W0 per layer.  The step-time difference is what the
+    re-reads of a shared W0 save (Infinity Cache or L2 hits).
+      gemma3-1b shapes, 26 layers: G=13 (two layers per band) vs G=26;
+      gemma4-31b sliding shapes, 12 layers: G=1 (one band, as band 0 of the
+      G=5 bundle) vs G=12."""
+    import torch
+    import synth
+    import synth.device as sdev
+    out = []
+    for name, dims, L, (g_shared, g_distinct), r in (
+            ("gemma3-1b", dict(synth.workload(2).dims), 26, (13, 26), 32),
+            ("gemma4-31b-sliding", dict(synth.workload(4).dims), 12, (1, 12), 256)):
+        rec = {"shapes": name, "layers": L, "rank": r}
+        for label, G in (("shared", g_shared), ("distinct", g_distinct)):
+            wl = synth.custom(L, G, r, dims, cid=70 + G)
+            bundle = sdev.load(wl, dev)
+            step = Step(wl, bundle, 1, CALLS, dev)
+            t, g = time_graph(step, steps, warmup)
+            rec[label] = {"bands": G, "step_us": t * 1e6, "GBps": step.bytes_rd / t / 1e9,
+                          "bytes_band_unique": step.bytes_band_unique}
+            rec["bytes_read_per_step"] = step.bytes_rd
+            del g, step, bundle
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        rec["saving_us"] = rec["distinct"]["step_us"] - rec["shared"]["step_us"]
+        rec["saving_frac"] = rec["saving_us"] / rec["distinct"]["step_us"]
+        log(f"band reuse A/B {name}: shared {rec['shared']['step_us']:.1f} us, distinct "
+            f"{rec['distinct']['step_us']:.1f} us per step")
+        out.append(rec)
+    return out
+
+
+def profile_band_reuse(dev):
+    """For a rocprofv3 counter run: decode calls (T=1) in a fixed order, so
+    that the counters of each stream launch can be matched to a label (the
+    labels are printed in launch order).  Each case flushes the Infinity
+    Cache (a 1 GiB read), then runs a call on one layer and the same call on
+    another layer:
+      31B o (W0 88 MB, fits the 256 MB Infinity Cache) and gate|up (W0
+      462 MB, does not): layer 0 then layer 1 (same band, same W0), and
+      layer 0 then layer 12 (another band);
+      gemma3-1b shapes, model order over layers 0..3 (every call of layer 0,
+      then of layer 1, ...): G=13 (layers 2b, 2b+1 share W0) and G=26.
+    Ends with a plain 1 GiB device copy whose counters calibrate FETCH_SIZE."""
+    import torch
+    import synth
+    import synth.device as sdev
+    flush_buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    labels = []
+
+    def flush():
+        flush_buf.sum()
+
+    def call(b, wl, layer, name, tag):
+        x = wl.x(layer, name, 1, dev)
+        if name in ("qkv", "gate_up"):
+            b.stacked(layer, name, x)
+        else:
+            b.linear(layer, name, x)
+        labels.append(tag)
+
+    wl4 = synth.workload(4)
+    b4 = sdev.load(wl4, dev)
+    torch.cuda.synchronize()
+    for name in ("o", "gate_up"):
+        for rep in range(2):
+            flush()
+            call(b4, wl4, 0, name, f"31b {name} L0 cold")
+            call(b4, wl4, 1, name, f"31b {name} L1 same band")
+            flush()
+            call(b4, wl4, 0, name, f"31b {name} L0 cold")
+            call(b4, wl4, 12, name, f"31b {name} L12 other band")
+    del b4
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    for G in (13, 26):
+        wl = synth.custom(26, G, 32, dict(synth.workload(2).dims), cid=70 + G)
+        b = sdev.load(wl, dev)
+        torch.cuda.synchronize()
+        flush()
+        for layer in range(4):
+            for name, _ in CALLS:
+                call(b, wl, layer, name, f"gemma3 G{G} {name} L{layer}")
+        del b
+        torch.cuda.synchronize()
+    src = torch.ones(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": "band-reuse", "stream_launch_labels": labels, "copy_bytes": src.numel() * 2}),
+          flush=True)
+
+
 def decompose_flops(m, n, k, rank, over, q):
     """Algorithmic fp32 flops of the GPU decomposition of one band: per layer
     the products with the residual (R Omega, q rounds of R^T Y and R Z,
@@ -599,12 +844,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill", "dense", "act", "fp8",
-                                                             "decompose"])
+                                                             "decompose", "small", "reuse"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--band-reuse", action="store_true",
                     help="report whether a band-shared W0 re-read by the next layer is served from the 256 MB "
                          "Infinity Cache or from HBM (prints one JSON line)")
-    ap.add_argument("--profile", choices=["decode", "prefill"],
+    ap.add_argument("--profile", choices=["decode", "prefill", "band-reuse"],
                     help="for rocprofv3 counter runs: one eager step (decode: the headline workload at T=1; "
                          "prefill: the Gemma-4-31B mixed prefill at T=512), then a plain 1 GiB device copy whose "
                          "counters calibrate FETCH_SIZE / WRITE_SIZE")
@@ -623,6 +868,9 @@ def main():
     binding.lib()
 
     wl4 = synth.workload(4)
+    if args.profile == "band-reuse":
+        profile_band_reuse(dev)
+        return
     if args.profile:
         import synth.device as sdev
         wlp, T = (wl4, 1) if args.profile == "decode" else (synth.workload(5), 512)
@@ -679,6 +927,12 @@ def main():
         res["prefill3_stacked"] = prefill_section(synth.workload(3), 2048, CALLS, args.steps, args.warmup, dev)
         log(f"prefill w3, stacked calls: {res['prefill3_stacked']['TFLOPs']:.1f} TFLOP/s")
 
+    if args.only in ("all", "small"):
+        res["workload1"] = workload1_section(dev, args.steps, args.warmup)
+        log(f"one-family workload: cold {res['workload1']['cold_us_per_call']:.2f} us, warm "
+            f"{res['workload1']['warm_us_per_call']:.2f} us per call")
+    if args.only in ("all", "reuse"):
+        res["band_reuse_ab"] = band_reuse_ab(dev, args.steps, args.warmup)
     if args.only in ("all", "decompose"):
         res["decompose_gemma3"] = decompose_section(dev, cpu_budget=0.0 if args.no_cpu else 4.0)
         log(f"decomposition: {res['decompose_gemma3']['matrices_per_s']:.1f} matrices/s, "
@@ -729,6 +983,12 @@ def main():
     if not args.no_cpu and args.only in ("all", "decode"):
         log("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(wl4, 1, args.cpu_budget, dev)
+    if not args.no_cpu and args.only in ("all", "prefill") and "prefill" in line:
+        log("cpu baseline, prefill")
+        line["prefill"]["cpu_baseline"] = oracle_prefill_baselines(dev)
+    if not args.no_cpu and args.only in ("all", "small"):
+        log("cpu baseline, small workloads")
+        res["oracle_small_decode"] = oracle_small_decode_baselines(dev)
     print(json.dumps(line), flush=True)
 
 

@@ -236,6 +236,33 @@ def test_split_k_prefill(gpu_lib, T):
             assert res["ok"], f"layer {layer} {c}: {res}"
 
 
+@pytest.mark.parametrize("rank", [5, 70])
+def test_long_k_decode_splits_vt(gpu_lib, rank):
+    """At T = 1 with an FP8 shared block a K of 16384 or more splits the V^T
+    rows in two K slices whose fp32 partials the epilogue adds (bf16 keeps
+    them whole): ragged rows and ranks, single and stacked calls, both
+    formats, against the oracle."""
+    dims = {(0, "q"): (136, 16392), (0, "k"): (40, 16392), (0, "v"): (40, 16392), (0, "o"): (16392, 136),
+            (0, "gate"): (72, 16384), (0, "up"): (72, 16384), (0, "down"): (16384, 72)}
+    wl = synth.custom(2, 1, rank, dims, cid=79)
+    for fmt in ("bf16", "fp8"):
+        ow = OracleWorkload(wl, DEV, w0_format=fmt)
+        b = sdev.load(wl, DEV, w0_format=fmt)
+        for layer in range(2):
+            for c in ("qkv", "gate_up", "q", "k", "gate"):
+                x = wl.x(layer, c, 1, DEV)
+                announce(f"long-K decode r={rank} {fmt} layer {layer} {c}")
+                y = call(b, layer, c, x)
+                torch.cuda.synchronize()
+                res = compare(np64(y), ow.call(layer, c, np64(x)))
+                assert res["ok"], f"{fmt} layer {layer} {c}: {res}"
+            x = wl.x(layer, "gate_up", 1, DEV)
+            h = b.gate_up_act(layer, "gelu_tanh", x)
+            torch.cuda.synchronize()
+            res = compare(np64(h), ow.gate_up_act(layer, np64(x), "gelu_tanh"))
+            assert res["ok"], f"{fmt} layer {layer} gate_up_act: {res}"
+
+
 @pytest.mark.parametrize("T", [40, 200])
 def test_split_k_finish_with_unaligned_scale(gpu_lib, T):
     """A single-family call's s is a row slice of its group's s: after a q of

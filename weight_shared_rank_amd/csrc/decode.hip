@@ -97,6 +97,12 @@ constexpr int kTargetWgsRows = WL_DECODE_TARGET_WGS_ROWS;
 // slices of 42 k-steps instead of 8 of 21)
 constexpr int kTargetWgsRows4 = WL_DECODE_TARGET_WGS_ROWS4;
 constexpr int kFp8Unroll = WL_FP8_UNROLL;
+// with an FP8 W0 the one-tile stream launch splits V^T rows in two K slices
+// from this K on
+#ifndef WL_VT_SPLIT_K
+#define WL_VT_SPLIT_K 16384
+#endif
+constexpr int kVtSplitK = WL_VT_SPLIT_K;
 
 // One batch of UNROLL complete k-steps (32 k each): loads first, then MFMAs.
 template <int UNROLL>
@@ -157,21 +163,78 @@ __device__ __forceinline__ void kblock_fp8(f32x4 &acc, const uint8_t *arow, cons
   }
 }
 
+// z = V^T x of four ranks rb .. rb+3 of token t, from one V^T workgroup.
+// Unsplit (KSV == 1): stored as a bf16 pair, z_hi [T][Rz] = bf16(z) and then
+// z_lo [T][Rz] = bf16(z - z_hi) (~16 significant bits), the MFMA operands
+// of the epilogue.  Split over K into two slices (KSV == 2, long K): each
+// slice's fp32 partial at [slice][T][Rz]; the epilogue adds the two.
+__device__ __forceinline__ void store_z(void *zbuf, int KSV, int slice, int T, int Rz, int t, int rb, int nrows,
+                                        f32x4 v) {
+  if (KSV == 1) {
+    uint16_t *zh = static_cast<uint16_t *>(zbuf) + static_cast<size_t>(t) * Rz;
+    uint16_t *zl = zh + static_cast<size_t>(T) * Rz;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (rb + i < nrows) {
+        const uint16_t hi = f32_to_bf16(v[i]);
+        zh[rb + i] = hi;
+        zl[rb + i] = f32_to_bf16(v[i] - bf16_to_f32(hi));
+      }
+    }
+    return;
+  }
+  float *zp = static_cast<float *>(zbuf) + (static_cast<size_t>(slice) * T + t) * Rz;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (rb + i < nrows) zp[rb + i] = v[i];
+}
+
+// Eight consecutive ranks of z for one token (element offset `off` = token
+// * Rz + rank in the z region) as the epilogue's two MFMA B operands: the
+// stored bf16 pair (KSV == 1), or, split in two (KSV == 2), the sum of the
+// two fp32 slice partials (slice 0 first) split into hi = bf16(z) and
+// lo = bf16(z - hi).
+__device__ __forceinline__ void load_z8(const void *zbuf, int KSV, int T, int Rz, size_t off, u32x4 &h, u32x4 &l) {
+  if (KSV == 1) {
+    const uint16_t *zh = static_cast<const uint16_t *>(zbuf) + off;
+    h = ld16(zh);
+    l = ld16(zh + static_cast<size_t>(T) * Rz);
+    return;
+  }
+  const float *zp = static_cast<const float *>(zbuf) + off;
+  const size_t sst = static_cast<size_t>(T) * Rz;
+  const f32x4 a0 = *reinterpret_cast<const f32x4 *>(zp), b0 = *reinterpret_cast<const f32x4 *>(zp + 4);
+  const f32x4 a1 = *reinterpret_cast<const f32x4 *>(zp + sst), b1 = *reinterpret_cast<const f32x4 *>(zp + sst + 4);
+  const f32x4 za = a0 + a1, zb = b0 + b1;
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float z0 = i < 2 ? za[2 * i] : zb[2 * i - 4], z1 = i < 2 ? za[2 * i + 1] : zb[2 * i - 3];
+    const uint16_t h0 = f32_to_bf16(z0), h1 = f32_to_bf16(z1);
+    hw[i] = h0 | (static_cast<uint32_t>(h1) << 16);
+    lw[i] = f32_to_bf16(z0 - bf16_to_f32(h0)) | (static_cast<uint32_t>(f32_to_bf16(z1 - bf16_to_f32(h1))) << 16);
+  }
+  h = u32x4{hw[0], hw[1], hw[2], hw[3]};
+  l = u32x4{lw[0], lw[1], lw[2], lw[3]};
+}
+
 // 1-D grid: first the V^T tiles (full K, so z needs no summation later; they
 // are dispatched first and finish well inside the launch), then the W0 tiles,
 // each split into KS slices of K.
 // XL (FP8 W0 at T = 1): x staged in LDS (dynamic shared memory of
 // ceil(pairs / KS) * 128 bytes).
 template <int W, int UNROLL, bool XL = false>
-__global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_part, uint16_t *z_pair, int ntile_vt,
+__global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_part, void *zbuf, int nwg_vt, int KSV,
                                                         int KS) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const bool vt = static_cast<int>(blockIdx.x) < ntile_vt;
-  const int widx = blockIdx.x - ntile_vt;
-  const int row0 = (vt ? blockIdx.x : widx / KS) * 16;
-  const int slice = vt ? 0 : widx % KS;
-  const int nslices = vt ? 1 : KS;
+  // the first nwg_vt workgroups are the V^T tiles, KSV slices of K each;
+  // then the W0 tiles, KS slices each
+  const bool vt = static_cast<int>(blockIdx.x) < nwg_vt;
+  const int widx = blockIdx.x - nwg_vt;
+  const int row0 = (vt ? blockIdx.x / KSV : widx / KS) * 16;
+  const int slice = vt ? blockIdx.x % KSV : widx % KS;
+  const int nslices = vt ? KSV : KS;
   const uint16_t *mat = vt ? c.Vt : c.W0;  // (null for an FP8 bundle's W0 tiles, which read W0f8)
   const int nrows = vt ? c.Rz : c.Ntot;
   const int K = c.K;
@@ -263,17 +326,7 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
   for (int w = 1; w < W; ++w) tot += red[w][lane];
   // lane holds D[m = 4g + i][n = r16]: rows row0 + 4g + i, token r16
   if (vt) {
-    uint16_t *zh = z_pair + static_cast<size_t>(r16) * c.Rz;
-    uint16_t *zl = zh + static_cast<size_t>(c.T) * c.Rz;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = row0 + g * 4 + i;
-      if (row < nrows) {
-        const uint16_t hi = f32_to_bf16(tot[i]);
-        zh[row] = hi;
-        zl[row] = f32_to_bf16(tot[i] - bf16_to_f32(hi));
-      }
-    }
+    store_z(zbuf, KSV, slice, c.T, c.Rz, r16, row0 + g * 4, nrows, tot);
     return;
   }
   float *dst = p_part + (static_cast<size_t>(slice) * c.T + r16) * c.Ntot;
@@ -291,7 +344,7 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
 // once per R row blocks cuts the operand traffic into the CU from 2x to
 // (1 + 1/R)x the W0 bytes.  Waves 0..R-1 each reduce one tile.
 template <int W, int UNROLL, int R>
-__global__ __launch_bounds__(W * 64) void stream_rows_kernel(CallDesc c, float *p_part, uint16_t *z_pair,
+__global__ __launch_bounds__(W * 64) void stream_rows_kernel(CallDesc c, float *p_part, void *zbuf,
                                                              int ntile_vt, int KS) {
   static_assert(W >= R, "one reducing wave per tile");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -371,17 +424,7 @@ __global__ __launch_bounds__(W * 64) void stream_rows_kernel(CallDesc c, float *
   const int tile0 = row0 + 16 * b;
   // lane holds D[m = 4g + i][n = r16]: rows tile0 + 4g + i, token r16
   if (vt) {
-    uint16_t *zh = z_pair + static_cast<size_t>(r16) * c.Rz;
-    uint16_t *zl = zh + static_cast<size_t>(c.T) * c.Rz;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = tile0 + g * 4 + i;
-      if (row < nrows) {
-        const uint16_t hi = f32_to_bf16(tot[i]);
-        zh[row] = hi;
-        zl[row] = f32_to_bf16(tot[i] - bf16_to_f32(hi));
-      }
-    }
+    store_z(zbuf, 1, 0, c.T, c.Rz, r16, tile0 + g * 4, nrows, tot);
     return;
   }
   float *dst = p_part + (static_cast<size_t>(slice) * c.T + r16) * c.Ntot;
@@ -398,9 +441,11 @@ __global__ __launch_bounds__(W * 64) void stream_rows_kernel(CallDesc c, float *
 }
 
 // One workgroup per 16-row tile; its WE waves split the rank steps of U z.
-template <int WE>
-__global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const float *p_part, const uint16_t *z_pair,
-                                                           int KS) {
+// KSM >= KS bounds the K slices whose partials wave 0 holds (so a call
+// with few slices keeps few registers and more workgroups resident).
+template <int WE, int KSM>
+__global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const float *p_part, const void *zbuf,
+                                                           int KSV, int KS) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * 16;
@@ -412,7 +457,7 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
   // r16; they are summed (in slice order) only after the delta, so these
   // loads and those of U and z are in flight together.  Slices past KS are
   // not loaded; rows past Ntot re-read a valid address and are dropped.
-  f32x4 part[kDecodeMaxSlices];
+  f32x4 part[KSM];
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
   if (wave == 0 && tok_ok) {
     const size_t sstride = static_cast<size_t>(c.T) * c.Ntot;
@@ -422,7 +467,7 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
     if (rbase + 3 < c.Ntot && (c.Ntot & 3) == 0 &&
         ((reinterpret_cast<uintptr_t>(c.s) | reinterpret_cast<uintptr_t>(qrow)) & 15) == 0) {
 #pragma unroll
-      for (int s = 0; s < kDecodeMaxSlices; ++s)
+      for (int s = 0; s < KSM; ++s)
         part[s] = s < KS ? *reinterpret_cast<const f32x4 *>(pp + static_cast<size_t>(s) * sstride + rbase) : f32x4{0.f, 0.f, 0.f, 0.f};
       sc = *reinterpret_cast<const f32x4 *>(c.s + rbase);
       if (qrow) sc *= *reinterpret_cast<const f32x4 *>(qrow + rbase);
@@ -431,7 +476,7 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
       for (int i = 0; i < 4; ++i) {
         const int row = min(rbase + i, c.Ntot - 1);
 #pragma unroll
-        for (int s = 0; s < kDecodeMaxSlices; ++s) part[s][i] = s < KS ? pp[static_cast<size_t>(s) * sstride + row] : 0.f;
+        for (int s = 0; s < KSM; ++s) part[s][i] = s < KS ? pp[static_cast<size_t>(s) * sstride + row] : 0.f;
         sc[i] = c.s[row] * (qrow ? qrow[row] : 1.f);
       }
     }
@@ -446,9 +491,8 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
     if (ch.rpad == 0 || row0 >= ch.row_start + ch.N || row0 + 16 <= ch.row_start) continue;
     const bool in_child = arow_g >= ch.row_start && arow_g < ch.row_start + ch.N;
     const uint16_t *urow = ch.U + static_cast<size_t>(in_child ? arow_g - ch.row_start : 0) * ch.rpad + g * 8;
-    // z pair row of this lane's token (token 0 stands in for columns >= T)
-    const uint16_t *zh = z_pair + static_cast<size_t>(tok_ok ? r16 : 0) * c.Rz + ch.zoff + g * 8;
-    const uint16_t *zl = zh + static_cast<size_t>(c.T) * c.Rz;
+    // z of this lane's token (token 0 stands in for columns >= T)
+    const size_t zrow = static_cast<size_t>(tok_ok ? r16 : 0) * c.Rz + ch.zoff + g * 8;
     // kk and k1 are multiples of 32 and rpad is too, so a step is either
     // wholly inside the padded rank or wholly outside.  Every load is
     // unconditional (an outside step re-reads step kk) and issued before the
@@ -458,7 +502,9 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
       const bool in1 = k1 < ch.rpad;
       const int k1c = in1 ? k1 : kk;
       const u32x4 ua0 = ld16(urow + kk), ua1 = ld16(urow + k1c);
-      const u32x4 h0 = ld16(zh + kk), l0 = ld16(zl + kk), h1 = ld16(zh + k1c), l1 = ld16(zl + k1c);
+      u32x4 h0, l0, h1, l1;
+      load_z8(zbuf, KSV, c.T, c.Rz, zrow + kk, h0, l0);
+      load_z8(zbuf, KSV, c.T, c.Rz, zrow + k1c, h1, l1);
       const u32x4 a0 = in_child ? ua0 : zero4;
       const u32x4 a1 = (in1 && in_child) ? ua1 : zero4;
       dacc = mfma16x16x32(a0, tok_ok ? h0 : zero4, dacc);
@@ -476,7 +522,7 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
   for (int w = 1; w < WE; ++w) d += red[w][lane];
   f32x4 p = part[0];
 #pragma unroll
-  for (int s = 1; s < kDecodeMaxSlices; ++s)
+  for (int s = 1; s < KSM; ++s)
     if (s < KS) p += part[s];
 
   // lane holds D[m = 4g + i][n = r16]: rows rbase + i, token r16
@@ -516,10 +562,10 @@ __global__ __launch_bounds__(WE * 64) void epilogue_kernel(CallDesc c, const flo
 // s_j p_j + (U_gate z_gate)_j and up_j the same on row N_g + j (children 0 and
 // 1 of the call, N_g rows each).  One workgroup per 16 values of j; its WE
 // waves split the rank steps of both deltas.
-template <int WE>
+template <int WE, int KSM>
 __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const float *p_part,
-                                                               const uint16_t *z_pair, int KS, int act, uint16_t *h,
-                                                               int ldh) {
+                                                               const void *zbuf, int KSV, int KS, int act,
+                                                               uint16_t *h, int ldh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int Ng = c.ch[0].N;
@@ -530,7 +576,7 @@ __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const
   // wave 0: p partials (slices < KS) and s of rows j0 + 4g + i of both halves
   // (rows past N_g re-read row N_g - 1 of the half and are dropped); summed
   // after the deltas so all loads are in flight together
-  float part[2][kDecodeMaxSlices][4];
+  float part[2][KSM][4];
   float sc[2][4];
   if (wave == 0 && tok_ok) {
     const size_t sstride = static_cast<size_t>(c.T) * c.Ntot;
@@ -541,7 +587,7 @@ __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const
       for (int i = 0; i < 4; ++i) {
         const int row = c.ch[hf].row_start + min(j0 + 4 * g + i, Ng - 1);
 #pragma unroll
-        for (int s = 0; s < kDecodeMaxSlices; ++s)
+        for (int s = 0; s < KSM; ++s)
           part[hf][s][i] = s < KS ? pp[static_cast<size_t>(s) * sstride + row] : 0.f;
         sc[hf][i] = c.s[row] * (c.q ? c.q[row] : 1.f);
       }
@@ -554,14 +600,15 @@ __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const
     const ChildDesc &ch = c.ch[hf];
     if (ch.rpad == 0) continue;
     const uint16_t *urow = ch.U + static_cast<size_t>(in_rows ? j0 + r16 : 0) * ch.rpad + g * 8;
-    const uint16_t *zh = z_pair + static_cast<size_t>(tok_ok ? r16 : 0) * c.Rz + ch.zoff + g * 8;
-    const uint16_t *zl = zh + static_cast<size_t>(c.T) * c.Rz;
+    const size_t zrow = static_cast<size_t>(tok_ok ? r16 : 0) * c.Rz + ch.zoff + g * 8;
     for (int kk = wave * 32; kk < ch.rpad; kk += 2 * WE * 32) {
       const int k1 = kk + WE * 32;
       const bool in1 = k1 < ch.rpad;
       const int k1c = in1 ? k1 : kk;
       const u32x4 ua0 = ld16(urow + kk), ua1 = ld16(urow + k1c);
-      const u32x4 h0 = ld16(zh + kk), l0 = ld16(zl + kk), h1 = ld16(zh + k1c), l1 = ld16(zl + k1c);
+      u32x4 h0, l0, h1, l1;
+      load_z8(zbuf, KSV, c.T, c.Rz, zrow + kk, h0, l0);
+      load_z8(zbuf, KSV, c.T, c.Rz, zrow + k1c, h1, l1);
       const u32x4 a0 = in_rows ? ua0 : zero4;
       const u32x4 a1 = (in1 && in_rows) ? ua1 : zero4;
       dacc[hf] = mfma16x16x32(a0, tok_ok ? h0 : zero4, dacc[hf]);
@@ -585,7 +632,7 @@ __global__ __launch_bounds__(WE * 64) void act_epilogue_kernel(CallDesc c, const
     for (int i = 0; i < 4; ++i) {
       float p = part[hf][0][i];
 #pragma unroll
-      for (int s = 1; s < kDecodeMaxSlices; ++s)
+      for (int s = 1; s < KSM; ++s)
         if (s < KS) p += part[hf][s][i];
       y[hf][i] = sc[hf][i] * p + d[i];
     }
@@ -625,10 +672,23 @@ int k_slices_for(int Ntot, int Rz, int K, int target) {
 
 int decode_k_slices(int Ntot, int Rz, int K) { return k_slices_for(Ntot, Rz, K, kTargetWgs); }
 
-hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream, int act,
+template <int KSM>
+hipError_t launch_epilogue(const CallDesc &c, const float *p_part, const void *zbuf, int KSV, int KS,
+                           hipStream_t stream, int act, uint16_t *h, int ldh) {
+  if (act < 0) {
+    hipLaunchKernelGGL((epilogue_kernel<kEpiWaves, KSM>), dim3((c.Ntot + 15) / 16), dim3(kEpiWaves * 64), 0, stream,
+                       c, p_part, zbuf, KSV, KS);
+  } else {
+    hipLaunchKernelGGL((act_epilogue_kernel<kEpiWaves, KSM>), dim3((c.ch[0].N + 15) / 16), dim3(kEpiWaves * 64), 0,
+                       stream, c, p_part, zbuf, KSV, KS, act, h, ldh);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStream_t stream, int act,
                          uint16_t *h, int ldh) {
   const int nt_w0 = (c.Ntot + 15) / 16;
-  int KS;
+  int KS, KSV = 1;
   const int KS1 = decode_k_slices(c.Ntot, c.Rz, c.K);
   constexpr int R = kStreamRows, R4 = 2 * kStreamRows;
   const int ks_rows = min(KS1, k_slices_for(c.Ntot, c.Rz, c.K, kTargetWgsRows));
@@ -667,28 +727,29 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hip
                        dim3(2 * kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
   } else {
     KS = c.W0f8 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV) : decode_k_slices(c.Ntot, c.Rz, c.K);
-    const int nt_vt = (c.Rz + 15) / 16;
+    // with an FP8 W0 the W0 workgroups stream half the bytes, and over a
+    // long K (>= kVtSplitK) a V^T tile over the whole K is the last
+    // workgroup still streaming: its rows are then split in two K slices
+    // (FP8 down call 40.1 -> 33.7 us; with bf16 W0 the split saved less in
+    // the stream launch than the epilogue's extra z loads cost)
+    KSV = (c.W0f8 != nullptr && c.K >= kVtSplitK && KS >= 2) ? 2 : 1;
+    const int nwg_vt = (c.Rz + 15) / 16 * KSV;
     if (c.T == 1 && c.W0f8 != nullptr) {
       const int npairs = (c.K + 63) / 64, pper = (npairs + KS - 1) / KS;
-      hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll, true>), dim3(nt_vt + nt_w0 * KS),
-                         dim3(kStreamWaves * 64), static_cast<size_t>(pper) * 128, stream, c, p_part, z_pair, nt_vt,
-                         KS);
+      hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll, true>), dim3(nwg_vt + nt_w0 * KS),
+                         dim3(kStreamWaves * 64), static_cast<size_t>(pper) * 128, stream, c, p_part, z_pair, nwg_vt,
+                         KSV, KS);
     } else {
-      hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nt_vt + nt_w0 * KS),
-                         dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
+      hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nwg_vt + nt_w0 * KS),
+                         dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nwg_vt, KSV, KS);
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (act < 0) {
-    hipLaunchKernelGGL((epilogue_kernel<kEpiWaves>), dim3(nt_w0), dim3(kEpiWaves * 64), 0, stream, c,
-                       static_cast<const float *>(p_part), static_cast<const uint16_t *>(z_pair), KS);
-  } else {
-    const int nt = (c.ch[0].N + 15) / 16;
-    hipLaunchKernelGGL((act_epilogue_kernel<kEpiWaves>), dim3(nt), dim3(kEpiWaves * 64), 0, stream, c,
-                       static_cast<const float *>(p_part), static_cast<const uint16_t *>(z_pair), KS, act, h, ldh);
-  }
-  return hipGetLastError();
+  const float *pp = static_cast<const float *>(p_part);
+  if (KS <= 2) return launch_epilogue<2>(c, pp, z_pair, KSV, KS, stream, act, h, ldh);
+  if (KS <= 4) return launch_epilogue<4>(c, pp, z_pair, KSV, KS, stream, act, h, ldh);
+  return launch_epilogue<kDecodeMaxSlices>(c, pp, z_pair, KSV, KS, stream, act, h, ldh);
 }
 
 }  // namespace wl

@@ -45,13 +45,14 @@ struct CallDesc {
 };
 
 // Decode path (T <= 16): launch 1 streams [W0; V^T] x into the K-slice
-// partials p_part [KS][T][Ntot] (fp32) and z = V^T x (V^T rows are not
-// split) as a bf16 hi/lo pair z_pair [2][T][Rz]; launch 2 sums the partials
-// and applies the scale and the U z epilogue.
+// partials p_part [KS][T][Ntot] (fp32) and z = V^T x into zbuf: a bf16
+// hi/lo pair [2][T][Rz] when the V^T rows run over the whole K, or two fp32
+// slice partials [2][T][Rz] when a long K splits them; launch 2 sums the
+// partials and applies the scale and the U z epilogue.
 // act >= 0: the call is gate|up (children 0 and 1 with equal N) and the
 // epilogue writes h [T][ldh] = act(gate) * up instead of y.
 int decode_k_slices(int Ntot, int Rz, int K);
-hipError_t launch_decode(const CallDesc &c, float *p_part, uint16_t *z_pair, hipStream_t stream, int act = -1,
+hipError_t launch_decode(const CallDesc &c, float *p_part, void *zbuf, hipStream_t stream, int act = -1,
                          uint16_t *h = nullptr, int ldh = 0);
 
 // Prefill path (T > 16): Z = X V into zbuf [T][Rz] (bf16), then the main

@@ -112,30 +112,42 @@ struct GemmArgs {
   int32_t ldh;
   int32_t nchild;
   ChildDesc ch[kMaxChildren];
+  // fused thin reduction (gemm_fz_kernel): V^T rows [rz][ldv] of the call
+  const uint16_t *Vt;
+  int64_t ldv;
+  int32_t rz;
 };
 
-template <int BM, int BN, int WM, int WN, int NST>
+// RZ > 0 (fused thin reduction): every stage also holds RZ rows of V^T
+// after the BM weight rows, and the waves accumulate Z = X V for the tile's
+// tokens beside the main product (FZ 16-rank fragments per wave).
+template <int BM, int BN, int WM, int WN, int NST, int RZ = 0>
 struct Tile {
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
-  static constexpr int GA = BM / 8, GB = BN / 8;  // 8-row load groups
+  static constexpr int AR = BM + RZ;               // A rows of a stage
+  static constexpr int FZ = RZ / 16 / WM;          // Z fragments per wave
+  static constexpr int GA = AR / 8, GB = BN / 8;  // 8-row load groups
   static constexpr int LPW = (GA + GB) / NW;      // LDS-DMA instructions per wave per stage
-  static constexpr int STAGE = (BM + BN) * kRowBytes;
+  static constexpr int STAGE = (AR + BN) * kRowBytes;
   static constexpr size_t LDS = static_cast<size_t>(NST) * STAGE;
   static_assert((GA + GB) % NW == 0, "8-row groups must split evenly over the waves");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tiles are whole MFMA blocks");
+  static_assert(RZ % (16 * WM) == 0, "the Z rows split evenly over the wave rows");
 };
 
 // One staged GEMM segment: acc += A B^T over 64-k steps [s_begin, s_end).
 // Row pointers are per load instruction (already offset to the lane's chunk);
 // a null row pointer reads the zero row.  klen bounds the valid k (chunks at
-// or past klen read the zero row).
-template <int BM, int BN, int WM, int WN, int NST>
-__device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
-                                        const uint16_t *const (&rp)[(BM + BN) / 8 / (WM * WN)], int klen,
-                                        int s_begin, int s_end, const uint16_t *zero_row, uint8_t *lds) {
-  using TL = Tile<BM, BN, WM, WN, NST>;
+// or past klen read the zero row).  With RZ > 0 the A rows BM .. BM+RZ-1 are
+// V^T rows whose products go to zacc.
+template <int BM, int BN, int WM, int WN, int NST, int RZ>
+__device__ __forceinline__ void segment_rz(f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
+                                           f32x4 (&zacc)[RZ ? RZ / 16 / WM : 1][BN / WN / 16],
+                                           const uint16_t *const (&rp)[(BM + RZ + BN) / 8 / (WM * WN)], int klen,
+                                           int s_begin, int s_end, const uint16_t *zero_row, uint8_t *lds) {
+  using TL = Tile<BM, BN, WM, WN, NST, RZ>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, g = lane >> 4;
@@ -145,7 +157,7 @@ __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16]
 #pragma unroll
   for (int q = 0; q < TL::LPW; ++q) {
     const int gq = wave * TL::LPW + q;
-    ldsoff[q] = gq < TL::GA ? gq * 1024 : BM * kRowBytes + (gq - TL::GA) * 1024;
+    ldsoff[q] = gq < TL::GA ? gq * 1024 : TL::AR * kRowBytes + (gq - TL::GA) * 1024;
   }
   // Running source pointers, one per load instruction, advanced by one stage
   // per issue (stages are issued in order); a lane without a row reads the
@@ -174,8 +186,10 @@ __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16]
   };
   auto issue = [&](int stage, int step) { issue_part(stage, step, 0, TL::LPW); };
   const int arow = (wm * TL::TM + r16) * kRowBytes;
-  const int brow = BM * kRowBytes + (wn * TL::TN + r16) * kRowBytes;
+  const int zrow = (BM + wm * TL::FZ * 16 + r16) * kRowBytes;
+  const int brow = TL::AR * kRowBytes + (wn * TL::TN + r16) * kRowBytes;
   const int sw0 = ((0 + g) ^ (r16 & 7)) * 16, sw1 = ((4 + g) ^ (r16 & 7)) * 16;
+  (void)zrow;
 
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
@@ -197,29 +211,66 @@ __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16]
     if (more) issue_part(nstage, nstep, 0, TL::LPW / 2);
     const uint8_t *sb = lds + (kt % NST) * TL::STAGE;
     // both halves' fragments are read up front (registers allow it: at most
-    // two waves per SIMD), so the LDS latency is paid once per stage
-    u32x4 fa[2][TL::FM], fb[2][TL::FN];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    // two waves per SIMD), so the LDS latency is paid once per stage; wave
+    // tiles of more than 16 MFMA blocks hold one half's fragments at a time
+    // (their accumulators leave no room for both)
+    constexpr bool kHalfFrags = TL::FM * TL::FN > 16;
+    constexpr int FH = kHalfFrags ? 1 : 2;
+    u32x4 fa[FH][TL::FM], fb[FH][TL::FN], fz[FH][TL::FZ ? TL::FZ : 1];
+    auto read_frags = [&](int h, int slot) __attribute__((always_inline)) {
       const int sw = h ? sw1 : sw0;
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i)
-        fa[h][i] = *reinterpret_cast<const u32x4 *>(sb + arow + i * 16 * kRowBytes + sw);
+        fa[slot][i] = *reinterpret_cast<const u32x4 *>(sb + arow + i * 16 * kRowBytes + sw);
+#pragma unroll
+      for (int i = 0; i < TL::FZ; ++i)
+        fz[slot][i] = *reinterpret_cast<const u32x4 *>(sb + zrow + i * 16 * kRowBytes + sw);
 #pragma unroll
       for (int j = 0; j < TL::FN; ++j)
-        fb[h][j] = *reinterpret_cast<const u32x4 *>(sb + brow + j * 16 * kRowBytes + sw);
+        fb[slot][j] = *reinterpret_cast<const u32x4 *>(sb + brow + j * 16 * kRowBytes + sw);
+    };
+    if constexpr (kHalfFrags) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        read_frags(h, 0);
+#pragma unroll
+        for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[0][i], fb[0][j], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < TL::FZ; ++i)
+#pragma unroll
+          for (int j = 0; j < TL::FN; ++j) zacc[i][j] = mfma16x16x32(fz[0][i], fb[0][j], zacc[i][j]);
+        if (h == 0 && more) issue_part(nstage, nstep, TL::LPW / 2, TL::LPW);
+      }
+      continue;
+    } else {
+      read_frags(0, 0);
+      read_frags(1, FH - 1);
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < FH; ++h) {
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i)
 #pragma unroll
         for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[h][i], fb[h][j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < TL::FZ; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) zacc[i][j] = mfma16x16x32(fz[h][i], fb[h][j], zacc[i][j]);
       if (h == 0 && more) issue_part(nstage, nstep, TL::LPW / 2, TL::LPW);
     }
   }
   // every wave is done with the ring before it is refilled
   __builtin_amdgcn_s_barrier();
+}
+
+template <int BM, int BN, int WM, int WN, int NST>
+__device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
+                                        const uint16_t *const (&rp)[(BM + BN) / 8 / (WM * WN)], int klen,
+                                        int s_begin, int s_end, const uint16_t *zero_row, uint8_t *lds) {
+  f32x4 none[1][BN / WN / 16];
+  segment_rz<BM, BN, WM, WN, NST, 0>(acc, none, rp, klen, s_begin, s_end, zero_row, lds);
 }
 
 // The two deltas of a paired gate|up tile in one pass.  Tile rows v < BM/2
@@ -574,6 +625,187 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 
   }
 }
 
+// Store a fused (non-paired) tile: rows f*BM + v, y through the child map
+// (four rows of one child with one 8-byte store, and its K=V copy).
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void store_fused_tile(const f32x4 (&acc)[BM / WM / 16][BN / WN / 16], const GemmArgs &a,
+                                                 int f, int n0) {
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN, r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int tok = n0 + wn * TN + j * 16 + r16;
+    if (tok >= a.T) continue;
+    uint16_t *yrow = a.Y + static_cast<int64_t>(tok) * a.ldy;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = f * BM + wm * TM + i * 16 + g * 4;
+      const int nv = max(0, min(4, a.M - row));
+      if (nv == 0) continue;
+      uint16_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(acc[i][j][e]);
+      int ci = 0;
+      while (ci + 1 < a.nchild && row >= a.ch[ci + 1].row_start) ++ci;
+      const ChildDesc &ch = a.ch[ci];
+      const int jj = row - ch.row_start;
+      uint16_t *p0 = yrow + ch.y_off + jj, *p1 = ch.dup_off >= 0 ? yrow + ch.dup_off + jj : p0;
+      if (nv == 4 && jj + 4 <= ch.N && ((reinterpret_cast<uintptr_t>(p0) | reinterpret_cast<uintptr_t>(p1)) & 7) == 0) {
+        const uint2 pk = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+        *reinterpret_cast<uint2 *>(p0) = pk;
+        if (ch.dup_off >= 0) *reinterpret_cast<uint2 *>(p1) = pk;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (e >= nv) break;
+          const int r = row + e;
+          int cj = ci;
+          while (cj + 1 < a.nchild && r >= a.ch[cj + 1].row_start) ++cj;
+          const ChildDesc &c2 = a.ch[cj];
+          const int j2 = r - c2.row_start;
+          yrow[c2.y_off + j2] = o[e];
+          if (c2.dup_off >= 0) yrow[c2.dup_off + j2] = o[e];
+        }
+      }
+    }
+  }
+}
+
+// One launch for a whole call with a small total rank (Rz <= RZ, RZ 64 or
+// 128): the workgroup of a BM x BN tile also computes its tokens' Z = X V.
+// Every stage of the main loop holds, after the BM rows of W0, the RZ rows
+// of V^T (rows past Rz read the zero row), so the X rows already staged for
+// the main product serve the thin reduction too; the waves accumulate
+// W0 x and V^T x side by side.  Then Z is rounded to bf16 (as between the
+// two launches of the unfused path) into LDS, token-major with 16-byte
+// chunk c of token t at slot c ^ (t % 8), the main accumulator is scaled by
+// s, and each child's U rows (A, streamed 64 ranks per step; ranks past the
+// child's padded rank read the zero row) multiply its columns of Z (B, from
+// LDS) into it before the bf16 store.  Each token tile's Z is recomputed by
+// every feature tile of its column: RZ / BM more MFMA work, traded for the
+// two launches (the Z product and its sum) it saves.
+template <int BM, int BN, int WM, int WN, int NST, int RZ>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_fz_kernel(GemmArgs a) {
+  using TL = Tile<BM, BN, WM, WN, NST, RZ>;
+  static_assert(RZ % 64 == 0, "Z rows are whole 64-rank blocks (the chunk swizzle stays inside a row)");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lrow & 7);
+  int f, sl, t;
+  unit_of(blockIdx.x, a.nM * a.nT, a.nT, 1, f, sl, t);
+  const int n0 = t * BN;
+
+  f32x4 acc[TL::FM][TL::FN], zacc[TL::FZ][TL::FN];
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < TL::FZ; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) zacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    const uint16_t *rp[TL::LPW];
+#pragma unroll
+    for (int q = 0; q < TL::LPW; ++q) {
+      const int gq = wave * TL::LPW + q;
+      if (gq < TL::GA) {
+        const int v = gq * 8 + lrow;
+        if (v < BM) {
+          const int row = f * BM + v;
+          rp[q] = row < a.M ? a.A + row * a.lda + lchunk * 8 : nullptr;
+        } else {
+          const int zr = v - BM;
+          rp[q] = zr < a.rz ? a.Vt + zr * a.ldv + lchunk * 8 : nullptr;
+        }
+      } else {
+        const int row = n0 + (gq - TL::GA) * 8 + lrow;
+        rp[q] = row < a.T ? a.B + row * a.ldb + lchunk * 8 : nullptr;
+      }
+    }
+    segment_rz<BM, BN, WM, WN, NST, RZ>(acc, zacc, rp, a.K, 0, (a.K + kBK - 1) / kBK, a.zero_row, lds);
+  }
+  // (the segment ends with a barrier: the ring is free)
+  // Z tile -> LDS: lane holds ranks wm*FZ*16 + 16i + 4g .. +3 of token
+  // wn*TN + 16j + r16
+  constexpr int ZROW = RZ * 2;  // bytes per token row
+#pragma unroll
+  for (int i = 0; i < TL::FZ; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) {
+      const int rk = wm * TL::FZ * 16 + i * 16 + g * 4;
+      const int tk = wn * TL::TN + j * 16 + r16;
+      const int off = tk * ZROW + (((rk >> 3) ^ (tk & 7)) << 4) + (rk & 4) * 2;
+      *reinterpret_cast<uint2 *>(lds + off) =
+          make_uint2(f32_to_bf16(zacc[i][j][0]) | (static_cast<uint32_t>(f32_to_bf16(zacc[i][j][1])) << 16),
+                     f32_to_bf16(zacc[i][j][2]) | (static_cast<uint32_t>(f32_to_bf16(zacc[i][j][3])) << 16));
+    }
+  // scale by s (rows outside the operand are never stored)
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) {
+    const int v = f * BM + wm * TL::TM + i * 16 + g * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sc = v + e < a.M ? a.s[v + e] : 0.f;
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j) acc[i][j][e] *= sc;
+    }
+  }
+  __syncthreads();
+  // delta: U rows of each child meeting the tile, 64 ranks per step
+  constexpr int ZBYTES = ((BN * ZROW + 1023) / 1024) * 1024;
+  static_assert(ZBYTES + BM * kRowBytes <= TL::LDS, "Z tile and one U stage fit the ring");
+  constexpr int GU = BM / 8, LPU = GU / TL::NW;
+  static_assert(GU % TL::NW == 0, "U rows split evenly over the waves");
+  uint8_t *ubuf = lds + ZBYTES;
+  const int arow = (wm * TL::TM + r16) * kRowBytes;
+  const int sw0 = ((0 + g) ^ (r16 & 7)) * 16, sw1 = ((4 + g) ^ (r16 & 7)) * 16;
+  for (int ci = 0; ci < a.nchild; ++ci) {
+    const ChildDesc &ch = a.ch[ci];
+    if (ch.rpad == 0 || f * BM >= ch.row_start + ch.N || f * BM + BM <= ch.row_start) continue;
+    for (int st = 0; st * kBK < ch.rpad; ++st) {
+#pragma unroll
+      for (int q = 0; q < LPU; ++q) {
+        const int gq = wave * LPU + q;
+        const int row = f * BM + gq * 8 + lrow;
+        const int k = st * kBK + lchunk * 8;
+        const bool in = row < a.M && row >= ch.row_start && row < ch.row_start + ch.N && k < ch.rpad;
+        const uint16_t *src = in ? ch.U + static_cast<int64_t>(row - ch.row_start) * ch.rpad + k : a.zero_row;
+        __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(ubuf + gq * 1024), 16, 0, 0);
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+      u32x4 fa[2][TL::FM], fb[2][TL::FN];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int sw = h ? sw1 : sw0;
+#pragma unroll
+        for (int i = 0; i < TL::FM; ++i)
+          fa[h][i] = *reinterpret_cast<const u32x4 *>(ubuf + arow + i * 16 * kRowBytes + sw);
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) {
+          const int tk = wn * TL::TN + j * 16 + r16;
+          // ranks past Rz (the last child's step beyond its padded rank) meet
+          // zero U columns; any chunk of the row serves as their operand
+          const int cz = ((((ch.zoff + st * kBK + h * 32) >> 3) + g) & (RZ / 8 - 1));
+          fb[h][j] = *reinterpret_cast<const u32x4 *>(lds + tk * ZROW + ((cz ^ (tk & 7)) << 4));
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[h][i], fb[h][j], acc[i][j]);
+      __syncthreads();  // every wave is done with ubuf before the next step refills it
+    }
+  }
+  store_fused_tile<BM, BN, WM, WN>(acc, a, f, n0);
+}
+
 // Z[i] = bf16(sum over slices of P[slice][i]), slices in order; n is a
 // multiple of 4 (T * Rz with Rz a multiple of 32).
 __global__ void reduce_z_kernel(const float *P, int ksplit, size_t n, uint16_t *Z) {
@@ -707,8 +939,12 @@ hipError_t launch_gemm_inst(const GemmArgs &a, hipStream_t stream) {
 
 template <int BM, int BN, int WM, int WN, int NST>
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
-  return (a.pair && a.nchild == 2) ? launch_gemm_inst<BM, BN, WM, WN, NST, true>(a, stream)
-                                   : launch_gemm_inst<BM, BN, WM, WN, NST, false>(a, stream);
+  // a paired gate|up tile stages BM + 2 BN rows twice in the ring; tiles
+  // where that does not fit are never planned for paired calls
+  if constexpr (2 * (BM + 2 * BN) <= NST * (BM + BN)) {
+    if (a.pair && a.nchild == 2) return launch_gemm_inst<BM, BN, WM, WN, NST, true>(a, stream);
+  }
+  return launch_gemm_inst<BM, BN, WM, WN, NST, false>(a, stream);
 }
 
 // Tile shapes: BM features x BN tokens.  eff ranks the shapes by measured
@@ -717,11 +953,27 @@ struct TileCfg {
   int BM, BN;
   double eff;
 };
-constexpr TileCfg kTiles[] = {{256, 128, 1.0}, {128, 128, 0.75}, {128, 64, 0.5}, {64, 64, 0.3}};
+// The largest tile (tuning builds may swap it; 0 is the default):
+//   0: 256 x 128 on eight waves (4 x 2, 64 x 64 each), three stages
+//   1: 256 x 128 on four waves (2 x 2, 128 x 64 each), three stages
+//   2: 256 x 256 on eight waves (4 x 2, 64 x 128 each), two stages
+//   3: 128 x 256 on eight waves (2 x 4, 64 x 64 each), three stages
+#ifndef WL_PREFILL_BIG
+#define WL_PREFILL_BIG 0
+#endif
+#ifndef WL_PREFILL_BIG_EFF
+#define WL_PREFILL_BIG_EFF 1.0
+#endif
+constexpr int kBigBM = WL_PREFILL_BIG == 2 ? 256 : (WL_PREFILL_BIG == 3 ? 128 : 256);
+constexpr int kBigBN = WL_PREFILL_BIG >= 2 ? 256 : 128;
+constexpr TileCfg kTiles[] = {{kBigBM, kBigBN, WL_PREFILL_BIG_EFF}, {128, 128, 0.75}, {128, 64, 0.5}, {64, 64, 0.3}};
+constexpr int kBigNst = WL_PREFILL_BIG == 2 ? 2 : 3;
+constexpr bool kBigPairs = 2 * (kBigBM + 2 * kBigBN) <= kBigNst * (kBigBM + kBigBN);
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 struct Plan {
   int tile, ksplit, steps_per_slice, nM, nT;
+  double cost;
 };
 
 // Choose the tile shape and the K split of one GEMM (M rows, K deep, T
@@ -733,14 +985,15 @@ struct Plan {
 // split the K steps plus the delta steps evenly, the last one taking that
 // many fewer K steps.  Unit: one 64-k step of a 256 x 128 tile (48 KB
 // streamed per CU).
-Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true) {
+Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true, bool skip_big = false) {
   const int nsteps = (K + kBK - 1) / kBK;
-  Plan best{kNumTiles - 1, 1, nsteps, (M + 63) / 64, (T + 63) / 64};
+  Plan best{kNumTiles - 1, 1, nsteps, (M + 63) / 64, (T + 63) / 64, 1e300};
   double best_cost = 1e300;
   // smallest tile first: on equal cost (latency-bound small GEMMs) the tile
   // that wastes no rows wins
   for (int i = kNumTiles - 1; i >= 0; --i) {
     if (i != kNumTiles - 1 && kTiles[i].BM >= 2 * M) continue;  // at least half the rows would be empty
+    if (i == 0 && skip_big) continue;
     const int nM = (M + kTiles[i].BM - 1) / kTiles[i].BM, nT = (T + kTiles[i].BN - 1) / kTiles[i].BN;
     const long tiles = static_cast<long>(nM) * nT;
     const double scale = std::max(kStepFloor, (kTiles[i].BM * kTiles[i].BN) / (256.0 * 128.0) / kTiles[i].eff);
@@ -764,7 +1017,7 @@ Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true) {
       }
       if (cost < best_cost) {
         best_cost = cost;
-        best = Plan{i, ks, per, nM, nT};
+        best = Plan{i, ks, per, nM, nT, cost};
       }
     }
   }
@@ -783,10 +1036,78 @@ hipError_t launch_planned(GemmArgs a, const Plan &p, hipStream_t stream) {
   a.ksplit = p.ksplit;
   a.steps_per_slice = p.steps_per_slice;
   switch (p.tile) {
+#if WL_PREFILL_BIG == 1
+    case 0: return launch_gemm<256, 128, 2, 2, 3>(a, stream);
+#elif WL_PREFILL_BIG == 2
+    case 0: return launch_gemm<256, 256, 4, 2, 2>(a, stream);
+#elif WL_PREFILL_BIG == 3
+    case 0: return launch_gemm<128, 256, 2, 4, 3>(a, stream);
+#else
     case 0: return launch_gemm<256, 128, 4, 2, 3>(a, stream);
+#endif
     case 1: return launch_gemm<128, 128, 4, 2, 4>(a, stream);
     case 2: return launch_gemm<128, 64, 2, 2, 4>(a, stream);
     default: return launch_gemm<64, 64, 2, 2, 4>(a, stream);
+  }
+}
+
+// Fused thin reduction (gemm_fz_kernel): tile shapes, the stage depth each
+// holds with RZ rows of V^T added, and their relative streaming efficiency.
+// The 256 x 128 tile has room for only two stages and measured slower than
+// the unfused path wherever the planner took it (the Gemma-3 gate and up
+// calls: 64 us against 56), so it is priced out.
+constexpr TileCfg kFzTiles[] = {{256, 128, 0.4}, {128, 128, 0.75}, {128, 64, 0.5}, {64, 64, 0.3}};
+constexpr int kNumFzTiles = sizeof(kFzTiles) / sizeof(kFzTiles[0]);
+// Cost of one more dependent launch, in the planner's units (a 64-k step of
+// a 256 x 128 tile): the unfused path's separate Z product.
+constexpr double kLaunch = 6.0;
+constexpr int kMaxFusedRank = 128;
+
+// The fused plan of a call with Rz total padded ranks (RZ = 64 or 128 rows of
+// V^T per stage): K unsplit; each step streams BM + RZ + BN rows instead of
+// BM + BN, and the tile adds its delta steps.
+Plan plan_fused_z(int M, int K, int T, int RZ, int dsteps) {
+  const int nsteps = (K + kBK - 1) / kBK;
+  Plan best{kNumFzTiles - 1, 1, nsteps, (M + 63) / 64, (T + 63) / 64, 1e300};
+  for (int i = kNumFzTiles - 1; i >= 0; --i) {
+    const TileCfg &tc = kFzTiles[i];
+    if (i != kNumFzTiles - 1 && tc.BM >= 2 * M) continue;
+    const int nM = (M + tc.BM - 1) / tc.BM, nT = (T + tc.BN - 1) / tc.BN;
+    const long rounds = (static_cast<long>(nM) * nT + kCUs - 1) / kCUs;
+    const double scale = std::max(kStepFloor, (tc.BM * tc.BN) / (256.0 * 128.0) / tc.eff);
+    const double stream = static_cast<double>(tc.BM + RZ + tc.BN) / (tc.BM + tc.BN);
+    const double cost = static_cast<double>(rounds) * (nsteps * stream + dsteps) * scale;
+    if (cost < best.cost) best = Plan{i, 1, nsteps, nM, nT, cost};
+  }
+  return best;
+}
+
+template <int BM, int BN, int WM, int WN, int NST, int RZ>
+hipError_t launch_fz_inst(const GemmArgs &a, hipStream_t stream) {
+  using TL = Tile<BM, BN, WM, WN, NST, RZ>;
+  auto kern = gemm_fz_kernel<BM, BN, WM, WN, NST, RZ>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(TL::LDS));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(a.nM * a.nT), dim3(WM * WN * 64), TL::LDS, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_z(GemmArgs a, const Plan &p, int RZ, hipStream_t stream) {
+  a.nM = p.nM;
+  a.nT = p.nT;
+  a.ksplit = 1;
+  a.steps_per_slice = p.steps_per_slice;
+  const bool r64 = RZ == 64;
+  switch (p.tile) {
+    case 0: return r64 ? launch_fz_inst<256, 128, 4, 2, 2, 64>(a, stream) : launch_fz_inst<256, 128, 4, 2, 2, 128>(a, stream);
+    case 1: return r64 ? launch_fz_inst<128, 128, 4, 2, 3, 64>(a, stream) : launch_fz_inst<128, 128, 4, 2, 3, 128>(a, stream);
+    case 2: return r64 ? launch_fz_inst<128, 64, 2, 2, 4, 64>(a, stream) : launch_fz_inst<128, 64, 2, 2, 3, 128>(a, stream);
+    default: return r64 ? launch_fz_inst<64, 64, 2, 2, 4, 64>(a, stream) : launch_fz_inst<64, 64, 2, 2, 4, 128>(a, stream);
   }
 }
 
@@ -799,6 +1120,8 @@ size_t partial_bytes(const Plan &p, int M, int T, bool delta) {
 size_t prefill_partial_bytes(int Ntot, int Rz, int rmax, int K, int T) {
   const int dsteps = (rmax + kBK - 1) / kBK;
   size_t n = partial_bytes(plan_gemm(Ntot, K, T, dsteps), Ntot, T, dsteps > 0);
+  if (!kBigPairs)  // the fused gate|up activation plans without the largest tile
+    n = std::max(n, partial_bytes(plan_gemm(Ntot, K, T, dsteps, true, true), Ntot, T, dsteps > 0));
   if (Rz > 0) n = std::max(n, partial_bytes(plan_gemm(Rz, K, T, 0), Rz, T, false));
   return n;
 }
@@ -806,6 +1129,37 @@ size_t prefill_partial_bytes(int Ntot, int Rz, int rmax, int K, int T) {
 hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const uint16_t *zero_row,
                           hipStream_t stream, int act, uint16_t *h, int ldh) {
   hipError_t e;
+  if (act < 0 && c.Rz > 0 && c.Rz <= kMaxFusedRank) {
+    // small total rank: one launch that computes each tile's Z itself, where
+    // the planner's estimate beats the separate Z product and its launches
+    const int RZ = c.Rz <= 64 ? 64 : 128;
+    const int dsteps = delta_steps(c);
+    const Plan pf = plan_fused_z(c.Ntot, c.K, c.T, RZ, dsteps);
+    const Plan pz = plan_gemm(c.Rz, c.K, c.T, 0);
+    const Plan pm = plan_gemm(c.Ntot, c.K, c.T, dsteps);
+    const double unfused = pz.cost + (pz.ksplit > 1 ? kSplitLaunch : 0.0) + pm.cost + kLaunch;
+    if (pf.cost < unfused) {
+      GemmArgs a{};
+      a.A = c.W0;
+      a.M = c.Ntot;
+      a.lda = c.K;
+      a.B = c.x;
+      a.T = c.T;
+      a.ldb = c.K;
+      a.K = c.K;
+      a.zero_row = zero_row;
+      a.mode = kFused;
+      a.Y = c.y;
+      a.ldy = c.ldy;
+      a.s = c.s;
+      a.Vt = c.Vt;
+      a.ldv = c.K;
+      a.rz = c.Rz;
+      a.nchild = c.nchild;
+      for (int i = 0; i < c.nchild; ++i) a.ch[i] = c.ch[i];
+      return launch_fused_z(a, pf, RZ, stream);
+    }
+  }
   if (c.Rz > 0) {
     GemmArgs a{};
     a.A = c.Vt;
@@ -849,7 +1203,7 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const 
   a.P = pbuf;
   a.nchild = c.nchild;
   for (int i = 0; i < c.nchild; ++i) a.ch[i] = c.ch[i];
-  Plan p = plan_gemm(c.Ntot, c.K, c.T, delta_steps(c));
+  Plan p = plan_gemm(c.Ntot, c.K, c.T, delta_steps(c), true, act >= 0 && !kBigPairs);
   if (act >= 0) {
     // gate|up with the activation fused: tiles hold BM/2 gate rows and the
     // matching BM/2 up rows

@@ -241,7 +241,8 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
 }
 
 // Workspace.  Decode (T <= 16): the stream launch's fp32 partials,
-// p_part [kDecodeMaxSlices][T][Nmax] (fp32) then z_pair [2][T][Rmax] (bf16).
+// p_part [kDecodeMaxSlices][T][Nmax] (fp32), then z: a bf16 pair or two fp32
+// slice partials, [2][T][Rmax] of 4-byte slots.
 // Prefill (T > 16): Z = X V as bf16 [T][Rmax].
 size_t ws_p_part_bytes(const Layout &lo, int32_t T) {
   return align256(static_cast<size_t>(wl::kDecodeMaxSlices) * T * lo.Nmax * 4);
@@ -283,8 +284,8 @@ size_t ws_w0_expand_bytes(const Layout &lo) {
 
 size_t ws_bytes_for(const Layout &lo, int32_t T) {
   size_t n;
-  if (T <= wl::kDecodeMaxT)
-    n = ws_p_part_bytes(lo, T) + align256(static_cast<size_t>(T) * lo.Rmax * 4);
+  if (T <= wl::kDecodeMaxT)  // z: a bf16 pair or two fp32 slices, [2][T][Rmax]
+    n = ws_p_part_bytes(lo, T) + align256(static_cast<size_t>(2) * T * lo.Rmax * 4);
   else
     n = ws_prefill_z_bytes(lo, T) + ws_prefill_partial_bytes(lo, T) + ws_w0_expand_bytes(lo);
   return n < 256 ? 256 : n;
@@ -418,8 +419,8 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
   hipError_t e;
   uint16_t *hout = act >= 0 ? static_cast<uint16_t *>(d_y) : nullptr;
   if (T <= wl::kDecodeMaxT)
-    e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), reinterpret_cast<uint16_t *>(ws + ws_p_part_bytes(h->lo, T)),
-                          s, act, hout, rv.out_dim);
+    e = wl::launch_decode(rv.c, reinterpret_cast<float *>(ws), ws + ws_p_part_bytes(h->lo, T), s, act, hout,
+                          rv.out_dim);
   else {
     // internal guard: this call's split partials fit the region sized for
     // the largest call shape of the bundle
