@@ -78,3 +78,70 @@ def quantize_rows(W0):
 def dequantize(codes, q):
     """value(c) * q, the W0 the quantized bundle stands for."""
     return E4M3[np.asarray(codes)] * np.asarray(q, np.float64)[:, None]
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (OCP Microscaling format, MXFP4): blocks of 32 consecutive elements of
+# a W0 row share one E8M0 scale X = 2^(b - 127) (b the stored byte); each
+# element is an E2M1 code.  The pages' quantized-shared-block headroom
+# ("Quality (Gemma 4 31B)" page, "Verdict": 4-bit shared blocks) in the
+# 4-bit microscaling format this part's matrix cores read.
+#
+# E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent field 0 is
+# the subnormal 0.m * 2^0.  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+#
+# Scale of a block (OCP MX): with amax its largest |w|, the shared exponent
+# is floor(log2(amax)) - 2 (2 = the largest E2M1 exponent), so amax / X lies
+# in [4, 8); elements are w / X (exact: X is a power of two) rounded to the
+# nearest E2M1 value, ties to the even mantissa, and clamped to +-6.  An
+# all-zero block takes X = 1.  Rows are padded with zeros to a multiple of 32.
+# ---------------------------------------------------------------------------
+MX_BLOCK = 32
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0],
+                np.float64)
+_E2M1_POS = E2M1[:8]
+
+
+def e2m1_encode(v):
+    """Nearest E2M1 code of each v (ties to the even mantissa: codes 0, 2,
+    4, 6), magnitudes above 6 clamped to 6; zero is code 0."""
+    v = np.asarray(v, np.float64)
+    a = np.minimum(np.abs(v), 6.0)
+    hi = np.clip(np.searchsorted(_E2M1_POS, a, side="left"), 0, 7)   # first value >= a
+    lo = np.clip(hi - 1, 0, 7)
+    dlo, dhi = a - _E2M1_POS[lo], _E2M1_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0) & (hi != lo))
+    mag = np.where(a == _E2M1_POS[hi], hi, np.where(pick_hi, hi, lo))
+    return (mag | np.where(np.signbit(v) & (mag != 0), 8, 0)).astype(np.uint8)
+
+
+def mx_exponent(amax):
+    """Shared exponent of a block with largest magnitude amax (0 if zero)."""
+    if amax == 0.0:
+        return 0
+    f, E = math.frexp(amax)          # amax = f * 2^E, f in [0.5, 1)
+    return (E - 1) - 2               # floor(log2 amax) - 2
+
+
+def quantize_mxfp4(W0):
+    """(codes [N, Kp] uint8 one code per element, scale bytes [N, Kp/32]
+    uint8) of a bf16-valued W0 [N, K]; Kp = K rounded up to 32."""
+    W0 = np.asarray(W0, np.float64)
+    N, K = W0.shape
+    Kp = (K + MX_BLOCK - 1) // MX_BLOCK * MX_BLOCK
+    W = np.zeros((N, Kp))
+    W[:, :K] = W0
+    blocks = W.reshape(N, Kp // MX_BLOCK, MX_BLOCK)
+    e = np.array([[mx_exponent(float(np.max(np.abs(b)))) for b in row] for row in blocks], np.int64)
+    b = np.clip(e + 127, 0, 254)
+    X = 2.0 ** (b - 127).astype(np.float64)
+    codes = e2m1_encode(blocks / X[:, :, None]).reshape(N, Kp)
+    return codes, b.astype(np.uint8)
+
+
+def dequantize_mxfp4(codes, scales, K):
+    """E2M1(code) * 2^(scale - 127) per element, the first K columns."""
+    codes = np.asarray(codes)
+    N, Kp = codes.shape
+    X = 2.0 ** (np.asarray(scales, np.int64) - 127).astype(np.float64)
+    return (E2M1[codes].reshape(N, Kp // MX_BLOCK, MX_BLOCK) * X[:, :, None]).reshape(N, Kp)[:, :K]

@@ -178,3 +178,44 @@ def test_resolution_mutants_are_caught(monkeypatch, name, target, attr, mutant):
         except (AssertionError, KeyError, ValueError):
             caught += 1
     assert caught >= 1, f"{name} passed every resolution pin"
+
+
+# --------------------------------------------------------------------------
+# MXFP4 quantizer
+# --------------------------------------------------------------------------
+from oracle import quant  # noqa: E402
+
+_orig_mx_exponent = quant.mx_exponent
+_orig_e2m1_encode = quant.e2m1_encode
+
+
+def _ceil_exponent(amax):
+    # scale from ceil(log2 amax) - 2: the block maximum lands in (2, 4]
+    import math
+    return 0 if amax == 0.0 else math.ceil(math.log2(amax)) - 2
+
+
+def _ties_away(v):
+    v = np.asarray(v, np.float64)
+    a = np.minimum(np.abs(v), 6.0)
+    mags = np.abs(quant.E2M1[:8])
+    d = np.abs(mags[None, :] - a.reshape(-1, 1))
+    idx = np.array([np.flatnonzero(row == row.min())[-1] for row in d])   # the larger on a tie
+    return (idx | np.where(np.signbit(v.reshape(-1)) & (idx != 0), 8, 0)).astype(np.uint8).reshape(v.shape)
+
+
+def _exponent_off_by_one(amax):
+    return _orig_mx_exponent(amax) + (1 if amax else 0)
+
+
+@pytest.mark.parametrize("attr,mutant", [("mx_exponent", _ceil_exponent), ("e2m1_encode", _ties_away),
+                                         ("mx_exponent", _exponent_off_by_one)])
+def test_mxfp4_mutants_are_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(quant, attr, mutant)
+    caught = 0
+    for pin in (pins.test_e2m1_rounding_brute_force, pins.test_mx_block_exponent_rule, pins.test_mxfp4_error_bound):
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"{mutant.__name__} passed every MXFP4 pin"

@@ -503,3 +503,81 @@ def test_quantized_rows_error_bound():
     assert np.all(Wq[3] == 0) and q[3] == 1.0
     m = np.max(np.abs(W), axis=1)[np.arange(64) != 3] / q[np.arange(64) != 3]
     assert np.all((m >= 224.0) & (m <= 448.0))
+
+
+# --------------------------------------------------------------------------
+# MXFP4 shared block (OCP microscaling: E2M1 elements, E8M0 scale per 32)
+# --------------------------------------------------------------------------
+def _e2m1_from_bits(code):
+    """E2M1 value from its bit fields: sign (bit 3), exponent (bits 2-1,
+    bias 1), mantissa (bit 0); exponent 0 is subnormal 0.m * 2^(1 - 1)."""
+    s = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    return s * (m * 0.5 if e == 0 else (1.0 + 0.5 * m) * 2.0 ** (e - 1))
+
+
+def test_e2m1_table_from_bit_fields():
+    from oracle import quant
+    assert [_e2m1_from_bits(c) for c in range(16)] == list(quant.E2M1)
+    assert quant.E2M1.max() == 6.0 and sorted(set(np.abs(quant.E2M1))) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_e2m1_rounding_brute_force():
+    """Nearest representable magnitude, ties to the even mantissa (code bit
+    0 clear), magnitudes above 6 clamped, by exhaustive search."""
+    from oracle import quant
+    rng = np.random.default_rng(11)
+    mags = np.array([_e2m1_from_bits(c) for c in range(8)])
+    ties = (mags[1:] + mags[:-1]) / 2
+    v = np.concatenate([rng.uniform(-8, 8, 3000), ties, -ties, [0.0, -0.0, 6.0, 7.9, -100.0]])
+    got = quant.e2m1_encode(v)
+    for x, c in zip(v, got):
+        a = min(abs(x), 6.0)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        want = want | (8 if (x < 0 and want != 0) else 0)
+        assert c == want, (x, c, want)
+
+
+def test_e8m0_scale_bytes_match_torch():
+    """A stored scale byte b stands for 2^(b - 127), as torch decodes E8M0."""
+    import torch
+    b = np.arange(0, 255, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.array_equal(ref, 2.0 ** (b.astype(np.int64) - 127))
+
+
+def test_mx_block_exponent_rule():
+    """The shared exponent puts the block maximum in [4, 8) times the scale
+    (brute-force search over exponents); all-zero blocks take scale 1."""
+    from oracle import quant
+    for a in [1.0, 4.0, 7.999, 8.0, 0.013, 2.0 ** -30, 3.0e5, 6.0, 5.99]:
+        e = quant.mx_exponent(a)
+        brute = [k for k in range(-200, 200) if 4.0 <= a / 2.0 ** k < 8.0]
+        assert brute == [e], (a, e, brute)
+    codes, scales = quant.quantize_mxfp4(np.zeros((2, 40)))
+    assert np.all(codes == 0) and np.all(scales == 127) and codes.shape == (2, 64) and scales.shape == (2, 2)
+
+
+def test_mxfp4_error_bound():
+    """Every element within one scale unit X of its value (the widest E2M1
+    gap, 4 to 6, halved) where |w/X| <= 6, within X/4 where |w/X| < 2; the
+    block maximum may reach 8X and then saturates to 6X (error < 2X); values
+    the format holds are exact; padding columns are zero codes."""
+    from oracle import quant
+    rng = np.random.default_rng(12)
+    W = rng.normal(0, 0.02, (16, 100))
+    W[5] = 0.0
+    W[6, :32] = 2.0 ** -7 * np.array([_e2m1_from_bits(c % 16) for c in range(32)])   # representable block
+    codes, scales = quant.quantize_mxfp4(W)
+    D = quant.dequantize_mxfp4(codes, scales, 100)
+    X = np.repeat(2.0 ** (scales.astype(np.int64) - 127), 32, axis=1)[:, :100]
+    err = np.abs(D - W)
+    r = np.abs(W) / X
+    assert np.all(err[r <= 6] <= X[r <= 6])
+    assert np.all((np.abs(D[r > 6]) == 6 * X[r > 6]) & (err[r > 6] < 2 * X[r > 6]))
+    small = r < 2.0
+    assert np.all(err[small] <= X[small] / 4)
+    assert np.array_equal(D[6, :32], W[6, :32]) and np.all(D[5] == 0)
+    assert np.all(codes[:, 100:] == 0)
