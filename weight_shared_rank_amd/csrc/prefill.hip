@@ -211,45 +211,23 @@ __device__ __forceinline__ void segment_rz(f32x4 (&acc)[BM / WM / 16][BN / WN / 
     if (more) issue_part(nstage, nstep, 0, TL::LPW / 2);
     const uint8_t *sb = lds + (kt % NST) * TL::STAGE;
     // both halves' fragments are read up front (registers allow it: at most
-    // two waves per SIMD), so the LDS latency is paid once per stage; wave
-    // tiles of more than 16 MFMA blocks hold one half's fragments at a time
-    // (their accumulators leave no room for both)
-    constexpr bool kHalfFrags = TL::FM * TL::FN > 16;
-    constexpr int FH = kHalfFrags ? 1 : 2;
-    u32x4 fa[FH][TL::FM], fb[FH][TL::FN], fz[FH][TL::FZ ? TL::FZ : 1];
-    auto read_frags = [&](int h, int slot) __attribute__((always_inline)) {
+    // two waves per SIMD), so the LDS latency is paid once per stage
+    u32x4 fa[2][TL::FM], fb[2][TL::FN], fz[2][TL::FZ ? TL::FZ : 1];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
       const int sw = h ? sw1 : sw0;
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i)
-        fa[slot][i] = *reinterpret_cast<const u32x4 *>(sb + arow + i * 16 * kRowBytes + sw);
+        fa[h][i] = *reinterpret_cast<const u32x4 *>(sb + arow + i * 16 * kRowBytes + sw);
 #pragma unroll
       for (int i = 0; i < TL::FZ; ++i)
-        fz[slot][i] = *reinterpret_cast<const u32x4 *>(sb + zrow + i * 16 * kRowBytes + sw);
+        fz[h][i] = *reinterpret_cast<const u32x4 *>(sb + zrow + i * 16 * kRowBytes + sw);
 #pragma unroll
       for (int j = 0; j < TL::FN; ++j)
-        fb[slot][j] = *reinterpret_cast<const u32x4 *>(sb + brow + j * 16 * kRowBytes + sw);
-    };
-    if constexpr (kHalfFrags) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        read_frags(h, 0);
-#pragma unroll
-        for (int i = 0; i < TL::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < TL::FN; ++j) acc[i][j] = mfma16x16x32(fa[0][i], fb[0][j], acc[i][j]);
-#pragma unroll
-        for (int i = 0; i < TL::FZ; ++i)
-#pragma unroll
-          for (int j = 0; j < TL::FN; ++j) zacc[i][j] = mfma16x16x32(fz[0][i], fb[0][j], zacc[i][j]);
-        if (h == 0 && more) issue_part(nstage, nstep, TL::LPW / 2, TL::LPW);
-      }
-      continue;
-    } else {
-      read_frags(0, 0);
-      read_frags(1, FH - 1);
+        fb[h][j] = *reinterpret_cast<const u32x4 *>(sb + brow + j * 16 * kRowBytes + sw);
     }
 #pragma unroll
-    for (int h = 0; h < FH; ++h) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i)
 #pragma unroll
@@ -939,12 +917,8 @@ hipError_t launch_gemm_inst(const GemmArgs &a, hipStream_t stream) {
 
 template <int BM, int BN, int WM, int WN, int NST>
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
-  // a paired gate|up tile stages BM + 2 BN rows twice in the ring; tiles
-  // where that does not fit are never planned for paired calls
-  if constexpr (2 * (BM + 2 * BN) <= NST * (BM + BN)) {
-    if (a.pair && a.nchild == 2) return launch_gemm_inst<BM, BN, WM, WN, NST, true>(a, stream);
-  }
-  return launch_gemm_inst<BM, BN, WM, WN, NST, false>(a, stream);
+  return (a.pair && a.nchild == 2) ? launch_gemm_inst<BM, BN, WM, WN, NST, true>(a, stream)
+                                   : launch_gemm_inst<BM, BN, WM, WN, NST, false>(a, stream);
 }
 
 // Tile shapes: BM features x BN tokens.  eff ranks the shapes by measured
@@ -953,22 +927,7 @@ struct TileCfg {
   int BM, BN;
   double eff;
 };
-// The largest tile (tuning builds may swap it; 0 is the default):
-//   0: 256 x 128 on eight waves (4 x 2, 64 x 64 each), three stages
-//   1: 256 x 128 on four waves (2 x 2, 128 x 64 each), three stages
-//   2: 256 x 256 on eight waves (4 x 2, 64 x 128 each), two stages
-//   3: 128 x 256 on eight waves (2 x 4, 64 x 64 each), three stages
-#ifndef WL_PREFILL_BIG
-#define WL_PREFILL_BIG 0
-#endif
-#ifndef WL_PREFILL_BIG_EFF
-#define WL_PREFILL_BIG_EFF 1.0
-#endif
-constexpr int kBigBM = WL_PREFILL_BIG == 2 ? 256 : (WL_PREFILL_BIG == 3 ? 128 : 256);
-constexpr int kBigBN = WL_PREFILL_BIG >= 2 ? 256 : 128;
-constexpr TileCfg kTiles[] = {{kBigBM, kBigBN, WL_PREFILL_BIG_EFF}, {128, 128, 0.75}, {128, 64, 0.5}, {64, 64, 0.3}};
-constexpr int kBigNst = WL_PREFILL_BIG == 2 ? 2 : 3;
-constexpr bool kBigPairs = 2 * (kBigBM + 2 * kBigBN) <= kBigNst * (kBigBM + kBigBN);
+constexpr TileCfg kTiles[] = {{256, 128, 1.0}, {128, 128, 0.75}, {128, 64, 0.5}, {64, 64, 0.3}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 struct Plan {
@@ -985,7 +944,7 @@ struct Plan {
 // split the K steps plus the delta steps evenly, the last one taking that
 // many fewer K steps.  Unit: one 64-k step of a 256 x 128 tile (48 KB
 // streamed per CU).
-Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true, bool skip_big = false) {
+Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true) {
   const int nsteps = (K + kBK - 1) / kBK;
   Plan best{kNumTiles - 1, 1, nsteps, (M + 63) / 64, (T + 63) / 64, 1e300};
   double best_cost = 1e300;
@@ -993,7 +952,6 @@ Plan plan_gemm(int M, int K, int T, int dsteps, bool allow_split = true, bool sk
   // that wastes no rows wins
   for (int i = kNumTiles - 1; i >= 0; --i) {
     if (i != kNumTiles - 1 && kTiles[i].BM >= 2 * M) continue;  // at least half the rows would be empty
-    if (i == 0 && skip_big) continue;
     const int nM = (M + kTiles[i].BM - 1) / kTiles[i].BM, nT = (T + kTiles[i].BN - 1) / kTiles[i].BN;
     const long tiles = static_cast<long>(nM) * nT;
     const double scale = std::max(kStepFloor, (kTiles[i].BM * kTiles[i].BN) / (256.0 * 128.0) / kTiles[i].eff);
@@ -1036,15 +994,7 @@ hipError_t launch_planned(GemmArgs a, const Plan &p, hipStream_t stream) {
   a.ksplit = p.ksplit;
   a.steps_per_slice = p.steps_per_slice;
   switch (p.tile) {
-#if WL_PREFILL_BIG == 1
-    case 0: return launch_gemm<256, 128, 2, 2, 3>(a, stream);
-#elif WL_PREFILL_BIG == 2
-    case 0: return launch_gemm<256, 256, 4, 2, 2>(a, stream);
-#elif WL_PREFILL_BIG == 3
-    case 0: return launch_gemm<128, 256, 2, 4, 3>(a, stream);
-#else
     case 0: return launch_gemm<256, 128, 4, 2, 3>(a, stream);
-#endif
     case 1: return launch_gemm<128, 128, 4, 2, 4>(a, stream);
     case 2: return launch_gemm<128, 64, 2, 2, 4>(a, stream);
     default: return launch_gemm<64, 64, 2, 2, 4>(a, stream);
@@ -1053,10 +1003,10 @@ hipError_t launch_planned(GemmArgs a, const Plan &p, hipStream_t stream) {
 
 // Fused thin reduction (gemm_fz_kernel): tile shapes, the stage depth each
 // holds with RZ rows of V^T added, and their relative streaming efficiency.
-// The 256 x 128 tile has room for only two stages and measured slower than
-// the unfused path wherever the planner took it (the Gemma-3 gate and up
-// calls: 64 us against 56), so it is priced out.
-constexpr TileCfg kFzTiles[] = {{256, 128, 0.4}, {128, 128, 0.75}, {128, 64, 0.5}, {64, 64, 0.3}};
+// (A 256 x 128 tile has room for only two stages with the V^T rows added,
+// spills registers, and measured slower than the unfused path on the
+// Gemma-3 gate and up calls: 64 us against 56; it is not offered.)
+constexpr TileCfg kFzTiles[] = {{128, 128, 0.75}, {128, 64, 0.5}, {64, 64, 0.3}};
 constexpr int kNumFzTiles = sizeof(kFzTiles) / sizeof(kFzTiles[0]);
 // Cost of one more dependent launch, in the planner's units (a 64-k step of
 // a 256 x 128 tile): the unfused path's separate Z product.
@@ -1104,9 +1054,8 @@ hipError_t launch_fused_z(GemmArgs a, const Plan &p, int RZ, hipStream_t stream)
   a.steps_per_slice = p.steps_per_slice;
   const bool r64 = RZ == 64;
   switch (p.tile) {
-    case 0: return r64 ? launch_fz_inst<256, 128, 4, 2, 2, 64>(a, stream) : launch_fz_inst<256, 128, 4, 2, 2, 128>(a, stream);
-    case 1: return r64 ? launch_fz_inst<128, 128, 4, 2, 3, 64>(a, stream) : launch_fz_inst<128, 128, 4, 2, 3, 128>(a, stream);
-    case 2: return r64 ? launch_fz_inst<128, 64, 2, 2, 4, 64>(a, stream) : launch_fz_inst<128, 64, 2, 2, 3, 128>(a, stream);
+    case 0: return r64 ? launch_fz_inst<128, 128, 4, 2, 3, 64>(a, stream) : launch_fz_inst<128, 128, 4, 2, 3, 128>(a, stream);
+    case 1: return r64 ? launch_fz_inst<128, 64, 2, 2, 4, 64>(a, stream) : launch_fz_inst<128, 64, 2, 2, 3, 128>(a, stream);
     default: return r64 ? launch_fz_inst<64, 64, 2, 2, 4, 64>(a, stream) : launch_fz_inst<64, 64, 2, 2, 4, 128>(a, stream);
   }
 }
@@ -1120,8 +1069,6 @@ size_t partial_bytes(const Plan &p, int M, int T, bool delta) {
 size_t prefill_partial_bytes(int Ntot, int Rz, int rmax, int K, int T) {
   const int dsteps = (rmax + kBK - 1) / kBK;
   size_t n = partial_bytes(plan_gemm(Ntot, K, T, dsteps), Ntot, T, dsteps > 0);
-  if (!kBigPairs)  // the fused gate|up activation plans without the largest tile
-    n = std::max(n, partial_bytes(plan_gemm(Ntot, K, T, dsteps, true, true), Ntot, T, dsteps > 0));
   if (Rz > 0) n = std::max(n, partial_bytes(plan_gemm(Rz, K, T, 0), Rz, T, false));
   return n;
 }
@@ -1203,7 +1150,7 @@ hipError_t launch_prefill(const CallDesc &c, uint16_t *zbuf, float *pbuf, const 
   a.P = pbuf;
   a.nchild = c.nchild;
   for (int i = 0; i < c.nchild; ++i) a.ch[i] = c.ch[i];
-  Plan p = plan_gemm(c.Ntot, c.K, c.T, delta_steps(c), true, act >= 0 && !kBigPairs);
+  Plan p = plan_gemm(c.Ntot, c.K, c.T, delta_steps(c));
   if (act >= 0) {
     // gate|up with the activation fused: tiles hold BM/2 gate rows and the
     // matching BM/2 up rows
