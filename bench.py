@@ -46,10 +46,20 @@ def log(msg):
     sys.stderr.flush()
 
 
+def w0_bytes(N, K, w0_format):
+    """Bytes of one W0 block: bf16 2NK; FP8 NK codes plus 4N of row scales;
+    MXFP4 NK/2 codes plus one scale byte per 32 elements."""
+    if w0_format == "fp8":
+        return N * K + 4 * N
+    if w0_format == "mxfp4":
+        return N * K // 2 + N * ((K + 31) // 32)
+    return 2 * N * K
+
+
 def call_bytes(wl, layer, fams, T, w0_format="bf16"):
-    """Algorithmic bytes a call must read: 2NK (W0) + 4N (s) + 2Nr (U) +
-    2Kr (V^T) per child, plus 2TK (x) once; and the bytes it writes (2TN).
-    An FP8 W0 is NK bytes of codes plus 4N of row scales."""
+    """Algorithmic bytes a call must read: W0 (2NK in bf16) + 4N (s) + 2Nr
+    (U) + 2Kr (V^T) per child, plus 2TK (x) once; and the bytes it writes
+    (2TN)."""
     lt = wl.layer_types[layer]
     rd = 0
     wr = 0
@@ -60,8 +70,7 @@ def call_bytes(wl, layer, fams, T, w0_format="bf16"):
             wr += 2 * T * N
             continue
         r = wl.clamped_rank(lt, f)
-        w0 = N * K + 4 * N if w0_format == "fp8" else 2 * N * K
-        rd += w0 + 4 * N + 2 * N * r + 2 * K * r
+        rd += w0_bytes(N, K, w0_format) + 4 * N + 2 * N * r + 2 * K * r
         wr += 2 * T * N
     return rd + 2 * T * K, wr
 
@@ -112,7 +121,7 @@ class Step:
                     key = (band_of_layer(layer, wl.num_layers, wl.num_bands), 0 if f in ("gate", "up", "down") else lt, f)
                     if key in seen_w0:
                         N, K = wl.shape(lt, f)
-                        self.bytes_band_unique -= N * K + 4 * N if w0_format == "fp8" else 2 * N * K
+                        self.bytes_band_unique -= w0_bytes(N, K, w0_format)
                     seen_w0.add(key)
                 self.bytes_wr += wr
                 self.flops += fl
@@ -899,6 +908,10 @@ def main():
         res["decode4_fp8_t1"] = decode_section(wl4, 1, args.steps, args.warmup, dev, w0_format="fp8")
         log(f"decode T=1, FP8 W0: {res['decode4_fp8_t1']['GBps']:.1f} GB/s, "
             f"{res['decode4_fp8_t1']['step_s'] * 1e3:.3f} ms per step")
+    if args.only in ("all", "decode", "fp8"):
+        res["decode4_mxfp4_t1"] = decode_section(wl4, 1, args.steps, args.warmup, dev, w0_format="mxfp4")
+        log(f"decode T=1, MXFP4 W0: {res['decode4_mxfp4_t1']['GBps']:.1f} GB/s, "
+            f"{res['decode4_mxfp4_t1']['step_s'] * 1e3:.3f} ms per step")
     if args.only in ("all", "decode", "dense"):
         res["dense_vs_weightless"] = dense_comparison(wl4, 1, 12, args.steps, args.warmup, dev)
         log(f"dense comparison: weightless {res['dense_vs_weightless']['weightless_ms']:.3f} ms, dense "

@@ -87,8 +87,17 @@ typedef enum { WL_SRC_W0 = 0, WL_SRC_S = 1, WL_SRC_U = 2, WL_SRC_V = 3 } wl_src_
  *    from bf16 device sources.  The bundle then stands for W0 = E4M3(code) * q
  *    (the quantized-shared-block variant, "Quality (Gemma 4 31B)" page,
  *    "Verdict"): decode reads one byte per W0 element; prefill and
- *    weightless_materialize expand the call's rows to bf16 in the workspace. */
-typedef enum { WL_W0_BF16 = 0, WL_W0_FP8 = 1 } wl_w0_format;
+ *    weightless_materialize expand the call's rows to bf16 in the workspace.
+ *    WL_W0_MXFP4 stores W0 in the OCP microscaling format MXFP4: each row
+ *    is cut into blocks of 32 elements (the row padded with zeros to a
+ *    multiple of 128) sharing one E8M0 scale X = 2^(b - 127), with b = e +
+ *    127 kept in [1, 254] and e = floor(log2(block max |w|)) - 2 (0 for an
+ *    all-zero block); each element is the E2M1 code nearest to w / X (ties
+ *    to the even mantissa, magnitudes clamped to 6), two codes per byte.
+ *    Coded by theta_bundle_load from bf16 device sources; decode reads half
+ *    a byte per W0 element plus one scale byte per 32, the GEMM paths expand
+ *    to bf16 as for FP8. */
+typedef enum { WL_W0_BF16 = 0, WL_W0_FP8 = 1, WL_W0_MXFP4 = 2 } wl_w0_format;
 typedef struct {
   int32_t num_layers;
   int32_t num_bands;

@@ -95,6 +95,9 @@ def dequantize(codes, q):
 # in [4, 8); elements are w / X (exact: X is a power of two) rounded to the
 # nearest E2M1 value, ties to the even mantissa, and clamped to +-6.  An
 # all-zero block takes X = 1.  Rows are padded with zeros to a multiple of 32.
+# The stored byte is kept in [1, 254] (a normal fp32 scale; byte 0 would be
+# the subnormal 2^-127 and 255 is NaN): a block whose maximum lies below
+# 2^-124 takes X = 2^-126 and keeps its elements within +-4.
 # ---------------------------------------------------------------------------
 MX_BLOCK = 32
 E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0],
@@ -132,8 +135,12 @@ def quantize_mxfp4(W0):
     W = np.zeros((N, Kp))
     W[:, :K] = W0
     blocks = W.reshape(N, Kp // MX_BLOCK, MX_BLOCK)
-    e = np.array([[mx_exponent(float(np.max(np.abs(b)))) for b in row] for row in blocks], np.int64)
-    b = np.clip(e + 127, 0, 254)
+    # mx_exponent of every block's amax; a bf16-valued W0 has few distinct
+    # block maxima, so the rule runs once per distinct value
+    amax = np.abs(blocks).max(axis=2)
+    vals, where = np.unique(amax, return_inverse=True)
+    e = np.array([mx_exponent(float(v)) for v in vals], np.int64)[where.reshape(amax.shape)]
+    b = np.clip(e + 127, 1, 254)
     X = 2.0 ** (b - 127).astype(np.float64)
     codes = e2m1_encode(blocks / X[:, :, None]).reshape(N, Kp)
     return codes, b.astype(np.uint8)

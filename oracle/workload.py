@@ -49,7 +49,8 @@ def w0_key(band, ltype, fam):
 class OracleWorkload:
     def __init__(self, wl, device="cpu", cache_w0=4, w0_format="bf16"):
         """w0_format "fp8": the bundle stands for W0 coded per row in E4M3
-        with a power-of-two scale (oracle.quant); every W0 the oracle uses is
+        with a power-of-two scale; "mxfp4": W0 coded in E2M1 with one E8M0
+        scale per 32 elements (oracle.quant); every W0 the oracle uses is
         that dequantized block."""
         self.wl = wl
         self.device = device
@@ -84,6 +85,8 @@ class OracleWorkload:
             w = to64(self.wl.w0(key[0], key[1], fam, self.device))
             if self.w0_format == "fp8":
                 w = quant.dequantize(*quant.quantize_rows(w))
+            elif self.w0_format == "mxfp4":
+                w = quant.dequantize_mxfp4(*quant.quantize_mxfp4(w), w.shape[1])
             self._w0[key] = w
         return self._w0[key]
 

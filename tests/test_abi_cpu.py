@@ -209,9 +209,14 @@ def test_fp8_spec_and_sources(L):
     n16, n8 = L.theta_bundle_arena_bytes(ctypes.byref(sp)), L.theta_bundle_arena_bytes(ctypes.byref(sp8))
     w0 = 4096 * 1152
     assert n16 - n8 == w0 - 4096 * 4
-    sp8.w0_format = 2
+    sp8.w0_format = 3
     assert L.theta_bundle_arena_bytes(ctypes.byref(sp8)) == 0
     assert "w0_format" in binding.last_error()
+    # MXFP4: half a byte per element (rows padded to 128 elements) and one
+    # E8M0 byte per 32 elements
+    sp4 = sdev.spec_of(wl, "mxfp4")
+    n4 = L.theta_bundle_arena_bytes(ctypes.byref(sp4))
+    assert n16 - n4 == 2 * w0 - (w0 // 2 + 4096 * 1152 // 32)
     sp8.w0_format = 1
     import numpy as np
     host = np.zeros((4096, 1152), np.uint16)

@@ -18,7 +18,7 @@ FAMILIES = ("q", "k", "v", "o", "gate", "up", "down")
 FAMILY = {f: i for i, f in enumerate(FAMILIES)}
 STACKS = {"qkv": 0, "gate_up": 1}
 ACTS = {"gelu_tanh": 0, "silu": 1, "gelu": 2}
-W0_FORMATS = {"bf16": 0, "fp8": 1}
+W0_FORMATS = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 WL_DTYPE_BF16, WL_DTYPE_F32 = 0, 1
 WL_SRC_W0, WL_SRC_S, WL_SRC_U, WL_SRC_V = 0, 1, 2, 3
 SRC_KIND = {"w0": WL_SRC_W0, "s": WL_SRC_S, "u": WL_SRC_U, "v": WL_SRC_V}

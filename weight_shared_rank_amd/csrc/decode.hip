@@ -97,6 +97,16 @@ constexpr int kTargetWgsRows = WL_DECODE_TARGET_WGS_ROWS;
 // slices of 42 k-steps instead of 8 of 21)
 constexpr int kTargetWgsRows4 = WL_DECODE_TARGET_WGS_ROWS4;
 constexpr int kFp8Unroll = WL_FP8_UNROLL;
+// MXFP4 W0: quads of 128 k per wave iteration, and the slice count is the
+// bf16 path's divided by kFp4KsDiv (a slice of codes is a quarter of the bytes)
+#ifndef WL_FP4_UNROLL
+#define WL_FP4_UNROLL 2
+#endif
+#ifndef WL_FP4_KS_DIV
+#define WL_FP4_KS_DIV 2
+#endif
+constexpr int kFp4Unroll = WL_FP4_UNROLL;
+constexpr int kFp4KsDiv = WL_FP4_KS_DIV;
 // with an FP8 W0 the one-tile stream launch splits V^T rows in two K slices
 // from this K on
 #ifndef WL_VT_SPLIT_K
@@ -135,6 +145,16 @@ __device__ __forceinline__ void fp8x16_to_bf16(u32x4 w, u32x4 &lo, u32x4 &hi) {
   }
   lo = u32x4{o[0], o[1], o[2], o[3]};
   hi = u32x4{o[4], o[5], o[6], o[7]};
+}
+
+// Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte
+// i) times their block scale sc -> one bf16 MFMA fragment.  Exact: an E2M1
+// value times a power of two inside the bf16 range.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t w, float sc) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3))};
 }
 
 // FP8 W0 rows: one 16-byte load per lane covers two 32-k MFMA steps.  Lane
@@ -221,8 +241,8 @@ __device__ __forceinline__ void load_z8(const void *zbuf, int KSV, int T, int Rz
 // 1-D grid: first the V^T tiles (full K, so z needs no summation later; they
 // are dispatched first and finish well inside the launch), then the W0 tiles,
 // each split into KS slices of K.
-// XL (FP8 W0 at T = 1): x staged in LDS (dynamic shared memory of
-// ceil(pairs / KS) * 128 bytes).
+// XL (FP8 or MXFP4 W0 at T = 1): x staged in LDS (dynamic shared memory of
+// the slice's x row: ceil(pairs / KS) * 128 or ceil(quads / KS) * 256 bytes).
 template <int W, int UNROLL, bool XL = false>
 __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_part, void *zbuf, int nwg_vt, int KSV,
                                                         int KS) {
@@ -235,7 +255,7 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
   const int row0 = (vt ? blockIdx.x / KSV : widx / KS) * 16;
   const int slice = vt ? blockIdx.x % KSV : widx % KS;
   const int nslices = vt ? KSV : KS;
-  const uint16_t *mat = vt ? c.Vt : c.W0;  // (null for an FP8 bundle's W0 tiles, which read W0f8)
+  const uint16_t *mat = vt ? c.Vt : c.W0;  // (null for a coded bundle's W0 tiles, which read W0f8 / W0f4)
   const int nrows = vt ? c.Rz : c.Ntot;
   const int K = c.K;
   const int nsteps = (K + 31) >> 5;
@@ -303,6 +323,57 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
       fp8x16_to_bf16(a, lo, hi);
       acc = mfma16x16x32(lo, tok_ok ? v0 : zero4, acc);
       acc = mfma16x16x32(hi, tok_ok ? v1 : zero4, acc);
+    }
+  } else if (!vt && c.W0f4) {
+    // MXFP4 W0: K in quads of 128 (four 32-element blocks, one per lane
+    // group); lane group g of quad p holds block 4p + g, k = 128p + 32g ..
+    // +31, whose four 8-code words feed four MFMA steps: step j takes k =
+    // 128p + 32g + 8j .. +7 (32 distinct k over the four lane groups), and x
+    // is loaded with the same assignment.  Slices split the quads; codes past
+    // K are zero (rows padded to a multiple of 128), x past K is not loaded.
+    const int nq = c.ldw0 / 64;
+    const int qper = (nq + KS - 1) / KS;
+    const int q_begin = min(nq, slice * qper), q_end = min(nq, q_begin + qper);
+    const uint8_t *arow4 = c.W0f4 + static_cast<size_t>(arow_idx) * c.ldw0 + g * 16;
+    const uint8_t *srow = c.sc4 + static_cast<size_t>(arow_idx) * c.ldsc + g;
+    const uint16_t *xrow4 = c.x + static_cast<size_t>(tok_ok ? r16 : 0) * K + g * 32;
+    constexpr int QU = kFp4Unroll;
+    // one token (XL): the slice's x row staged in LDS once per workgroup, so
+    // the loop issues one global load per 32 codes instead of five
+    extern __shared__ u32x4 xs[];
+    if constexpr (XL) {
+      const int nch = (q_end - q_begin) * 16;
+      for (int t = threadIdx.x; t < nch; t += W * 64) {
+        const int k = q_begin * 128 + t * 8;
+        xs[t] = k < K ? ld16(c.x + k) : zero4;
+      }
+      __syncthreads();
+    }
+    for (int q0 = q_begin + wave * QU; q0 < q_end; q0 += W * QU) {
+      u32x4 a[QU], xv[QU][4];
+      uint32_t b[QU];
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        const int qq = min(q0 + u, q_end - 1);  // a quad past the slice re-reads the last and is dropped
+        a[u] = *reinterpret_cast<const u32x4 *>(arow4 + static_cast<size_t>(qq) * 64);
+        b[u] = srow[static_cast<size_t>(qq) * 4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (XL) {
+            xv[u][j] = xs[(qq - q_begin) * 16 + g * 4 + j];
+          } else {
+            const int k = qq * 128 + g * 32 + j * 8;
+            xv[u][j] = k < K ? ld16(xrow4 + qq * 128 + j * 8) : zero4;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < QU; ++u) {
+        if (q0 + u >= q_end) break;
+        const float sc = __uint_as_float(b[u] << 23);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma16x16x32(fp4x8_to_bf16(a[u][j], sc), tok_ok ? xv[u][j] : zero4, acc);
+      }
     }
   } else {
     const uint16_t *arow = mat + static_cast<size_t>(arow_idx) * K + g * 8;
@@ -693,7 +764,7 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
   constexpr int R = kStreamRows, R4 = 2 * kStreamRows;
   const int ks_rows = min(KS1, k_slices_for(c.Ntot, c.Rz, c.K, kTargetWgsRows));
   const int ks_rows4 = min(KS1, k_slices_for(c.Ntot, c.Rz, c.K, kTargetWgsRows4));
-  if (c.W0f8 == nullptr && c.T >= kStreamRows4MinT && R4 * ks_rows4 <= kDecodeMaxSlices) {
+  if (c.W0 != nullptr && c.T >= kStreamRows4MinT && R4 * ks_rows4 <= kDecodeMaxSlices) {
     // eight or more tokens: R4 row tiles per W0 workgroup share each x
     // fragment (the x bytes pulled from L2 per W0 byte halve again), with R4
     // times the slices of the four-tile target; blocks of two k-steps
@@ -708,7 +779,7 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
     else
       hipLaunchKernelGGL((stream_rows_kernel<kStreamWaves, 1, R4>), dim3(nt_vt + nw_w0 * KS),
                          dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
-  } else if (c.W0f8 == nullptr && c.T >= kStreamRowsMinT && KS1 * R <= kDecodeMaxSlices) {
+  } else if (c.W0 != nullptr && c.T >= kStreamRowsMinT && KS1 * R <= kDecodeMaxSlices) {
     // several tokens: R row tiles per W0 workgroup share each x fragment,
     // with R times the slices of the lower several-token target (never more
     // than the R * KS1 <= kDecodeMaxSlices checked above)
@@ -716,7 +787,7 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
     const int nw_w0 = (c.Ntot + 16 * R - 1) / (16 * R), nt_vt = (c.Rz + 15) / 16;
     hipLaunchKernelGGL((stream_rows_kernel<kStreamWaves, kStreamUnroll, R>), dim3(nt_vt + nw_w0 * KS),
                        dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
-  } else if (c.W0f8 == nullptr && c.T >= kStreamWideMinT && KS1 == kDecodeMaxSlices &&
+  } else if (c.W0 != nullptr && c.T >= kStreamWideMinT && KS1 == kDecodeMaxSlices &&
              ((c.K + 31) / 32 + KS1 - 1) / KS1 >= 2 * kStreamWaves * 2) {
     // several tokens, long K slices (o- and down-shaped calls): R4 row tiles
     // per workgroup on twice the waves at the full slice count, in 2-step
@@ -726,19 +797,29 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
     hipLaunchKernelGGL((stream_rows_kernel<2 * kStreamWaves, 2, R4>), dim3(nt_vt + nw4 * KS),
                        dim3(2 * kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
   } else {
-    KS = c.W0f8 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV) : decode_k_slices(c.Ntot, c.Rz, c.K);
-    // with an FP8 W0 the W0 workgroups stream half the bytes, and over a
-    // long K (>= kVtSplitK) a V^T tile over the whole K is the last
-    // workgroup still streaming: its rows are then split in two K slices
-    // (FP8 down call 40.1 -> 33.7 us; with bf16 W0 the split saved less in
-    // the stream launch than the epilogue's extra z loads cost)
-    KSV = (c.W0f8 != nullptr && c.K >= kVtSplitK && KS >= 2) ? 2 : 1;
+    KS = c.W0f8   ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV)
+         : c.W0f4 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / kFp4KsDiv)
+                  : decode_k_slices(c.Ntot, c.Rz, c.K);
+    // with a coded W0 (FP8, MXFP4) the W0 workgroups stream a half or a
+    // quarter of the bytes, and over a long K (>= kVtSplitK) a V^T tile over
+    // the whole K is the last workgroup still streaming: its rows are then
+    // split in two K slices (FP8 down call 40.1 -> 33.7 us; with bf16 W0 the
+    // split saved less in the stream launch than the epilogue's extra z
+    // loads cost)
+    KSV = ((c.W0f8 != nullptr || c.W0f4 != nullptr) && c.K >= kVtSplitK && KS >= 2) ? 2 : 1;
     const int nwg_vt = (c.Rz + 15) / 16 * KSV;
-    if (c.T == 1 && c.W0f8 != nullptr) {
-      const int npairs = (c.K + 63) / 64, pper = (npairs + KS - 1) / KS;
+    if (c.T == 1 && (c.W0f8 != nullptr || c.W0f4 != nullptr)) {
+      // x slice in LDS: 64 k (128 bytes) per FP8 pair, 128 k per MXFP4 quad
+      size_t xbytes;
+      if (c.W0f8) {
+        const int npairs = (c.K + 63) / 64;
+        xbytes = static_cast<size_t>((npairs + KS - 1) / KS) * 128;
+      } else {
+        const int nq = c.ldw0 / 64;
+        xbytes = static_cast<size_t>((nq + KS - 1) / KS) * 256;
+      }
       hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll, true>), dim3(nwg_vt + nt_w0 * KS),
-                         dim3(kStreamWaves * 64), static_cast<size_t>(pper) * 128, stream, c, p_part, z_pair, nwg_vt,
-                         KSV, KS);
+                         dim3(kStreamWaves * 64), xbytes, stream, c, p_part, z_pair, nwg_vt, KSV, KS);
     } else {
       hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nwg_vt + nt_w0 * KS),
                          dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nwg_vt, KSV, KS);

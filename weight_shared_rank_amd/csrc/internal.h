@@ -35,7 +35,10 @@ struct CallDesc {
   const uint16_t *W0;  // [Ntot, K] bf16 (null for an FP8 bundle's decode call)
   const uint8_t *W0f8; // FP8 bundle: [Ntot, ldw0] E4M3 codes, else null
   const float *q;      // FP8 bundle: [Ntot] per-row scale of W0f8, else null
-  int32_t ldw0;        // row stride of W0f8 in bytes
+  int32_t ldw0;        // row stride of W0f8 / W0f4 in bytes
+  const uint8_t *W0f4; // MXFP4 bundle: [Ntot, ldw0] E2M1 codes, two per byte (element 2i low), else null
+  const uint8_t *sc4;  // MXFP4 bundle: [Ntot, ldsc] E8M0 scale bytes, one per 32 elements
+  int32_t ldsc;        // row stride of sc4 in bytes
   const float *s;      // [Ntot]
   const uint16_t *Vt;  // [Rz, K] bf16
   uint16_t *y;         // [T, ldy] bf16
@@ -80,6 +83,13 @@ hipError_t launch_quantize_rows(const uint16_t *src, int32_t N, int32_t K, uint8
                                 hipStream_t stream);
 hipError_t launch_dequantize_rows(const uint8_t *src, int32_t Kp, const float *q, int32_t N, int32_t K,
                                   uint16_t *dst, hipStream_t stream);
+// MXFP4 shared block: rows of src bf16 [N][K] -> E2M1 codes [N][Kq / 2]
+// (two per byte) and E8M0 block scales [N][Kq / 32] (Kq a multiple of 128,
+// padding zero codes), and back to bf16 [N][K].
+hipError_t launch_quantize_mxfp4(const uint16_t *src, int32_t N, int32_t K, uint8_t *codes, int32_t Kq,
+                                 uint8_t *scales, hipStream_t stream);
+hipError_t launch_dequantize_mxfp4(const uint8_t *codes, int32_t Kq, const uint8_t *scales, int32_t N, int32_t K,
+                                   uint16_t *dst, hipStream_t stream);
 
 // Decomposition (one band of one family): W0 = bf16(mean of the m layers
 // W [m][nk]); per layer s [N] (LS row scale, fp32) and R = W - s W0 (fp32

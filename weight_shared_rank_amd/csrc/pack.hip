@@ -2,7 +2,8 @@
 // padding reads as zero), the V [K, r] -> V^T [r, K] transpose, and the FP8
 // shared block: rows of W0 coded in OCP E4M3 with one power-of-two scale per
 // row (the quantized-shared-block variant, "Quality (Gemma 4 31B)" page,
-// "Verdict"), plus its expansion back to bf16 for the GEMM paths.
+// "Verdict"), the MXFP4 shared block (E2M1 codes, one E8M0 scale per 32
+// elements), and their expansion back to bf16 for the GEMM paths.
 #include "common.h"
 #include "internal.h"
 
@@ -83,10 +84,99 @@ __global__ void dequantize_rows_kernel(const uint8_t *src, int Kp, const float *
   const float qv = q[row];
   uint16_t *d = dst + static_cast<size_t>(row) * K;
   d[j] = f32_to_bf16(v[0] * qv);
-  d[j + 1] = f32_to_bf16(v[1] * qv);
+  if (j + 1 < K) d[j + 1] = f32_to_bf16(v[1] * qv);
+}
+
+// MXFP4 (OCP microscaling): one thread per block of 32 consecutive elements
+// of a row.  With amax the block's largest |w| = f * 2^E (f in [0.5, 1)),
+// the shared exponent is e = (E - 1) - 2 (so amax * 2^-e lies in [4, 8)),
+// 0 for an all-zero block; the stored E8M0 byte is b = e + 127 kept in
+// [1, 254].  Each element becomes the E2M1 code nearest to w * 2^(127 - b)
+// (exact scaling), ties to the even mantissa, magnitudes above 6 clamped:
+// |v| <= 0.25 -> 0, < 0.75 -> 0.5, <= 1.25 -> 1, < 1.75 -> 1.5, <= 2.5 -> 2,
+// < 3.5 -> 3, <= 5 -> 4, else 6 (codes 0..7, sign bit 8 for negative
+// nonzero codes).  Codes are packed two per byte, element 2i in the low
+// nibble; elements past K (row padding to Kq) are zero codes.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  uint32_t m = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.f ? 6u : 7u;
+  return (m != 0u && v < 0.f) ? (m | 8u) : m;
+}
+
+__global__ void quantize_mxfp4_kernel(const uint16_t *src, int N, int K, uint8_t *codes, int Kq, uint8_t *scales) {
+  const int nb = Kq / 32;
+  const long id = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (id >= static_cast<long>(N) * nb) return;
+  const int row = static_cast<int>(id / nb), blk = static_cast<int>(id % nb);
+  const uint16_t *w = src + static_cast<size_t>(row) * K;
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int j = blk * 32 + i;
+    v[i] = j < K ? bf16_to_f32(w[j]) : 0.f;
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  int e = 0;
+  if (amax > 0.f) {
+    int E;
+    frexpf(amax, &E);
+    e = E - 3;
+  }
+  const int b = min(254, max(1, e + 127));
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) out[i >> 3] |= e2m1_code(ldexpf(v[i], 127 - b)) << (4 * (i & 7));
+  uint32_t *d = reinterpret_cast<uint32_t *>(codes + static_cast<size_t>(row) * (Kq / 2) + blk * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = out[i];
+  scales[static_cast<size_t>(row) * nb + blk] = static_cast<uint8_t>(b);
+}
+
+// w[i][j] = E2M1(code) * 2^(b - 127) as bf16 (exact), eight elements per
+// thread, by the hardware conversion the decode kernel uses.
+__global__ void dequantize_mxfp4_kernel(const uint8_t *codes, int Kq, const uint8_t *scales, int N, int K,
+                                        uint16_t *dst) {
+  const int row = blockIdx.y;
+  const int j = 8 * (blockIdx.x * blockDim.x + threadIdx.x);
+  if (row >= N || j >= K) return;
+  const uint32_t word = *reinterpret_cast<const uint32_t *>(codes + static_cast<size_t>(row) * (Kq / 2) + j / 2);
+  const uint32_t b = scales[static_cast<size_t>(row) * (Kq / 32) + j / 32];
+  const float sc = __uint_as_float(b << 23);
+  uint16_t *d = dst + static_cast<size_t>(row) * K + j;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t pr;
+    switch (i) {
+      case 0: pr = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0)); break;
+      case 1: pr = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1)); break;
+      case 2: pr = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2)); break;
+      default: pr = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3)); break;
+    }
+    if (j + 2 * i < K) d[2 * i] = static_cast<uint16_t>(pr & 0xffffu);
+    if (j + 2 * i + 1 < K) d[2 * i + 1] = static_cast<uint16_t>(pr >> 16);
+  }
 }
 
 }  // namespace
+
+hipError_t launch_quantize_mxfp4(const uint16_t *src, int32_t N, int32_t K, uint8_t *codes, int32_t Kq,
+                                 uint8_t *scales, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const long n = static_cast<long>(N) * (Kq / 32);
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, src,
+                     N, K, codes, Kq, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_mxfp4(const uint8_t *codes, int32_t Kq, const uint8_t *scales, int32_t N, int32_t K,
+                                   uint16_t *dst, hipStream_t stream) {
+  if (N == 0 || K == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequantize_mxfp4_kernel, dim3(((K + 7) / 8 + 255) / 256, N), dim3(256), 0, stream, codes, Kq, scales,
+                     N, K, dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows(const uint16_t *src, int32_t N, int32_t K, uint8_t *dst, int32_t Kp, float *q,
                                 hipStream_t stream) {
@@ -98,7 +188,7 @@ hipError_t launch_quantize_rows(const uint16_t *src, int32_t N, int32_t K, uint8
 hipError_t launch_dequantize_rows(const uint8_t *src, int32_t Kp, const float *q, int32_t N, int32_t K,
                                   uint16_t *dst, hipStream_t stream) {
   if (N == 0 || K == 0) return hipSuccess;
-  hipLaunchKernelGGL(dequantize_rows_kernel, dim3((K / 2 + 255) / 256, N), dim3(256), 0, stream, src, Kp, q, K, dst);
+  hipLaunchKernelGGL(dequantize_rows_kernel, dim3(((K + 1) / 2 + 255) / 256, N), dim3(256), 0, stream, src, Kp, q, K, dst);
   return hipGetLastError();
 }
 

@@ -73,6 +73,7 @@ struct GroupShape {
   bool tied = false;  // QKV group on a K=V-tied type: the v slot copies k
   int K = 0;
   int Kp = 0;         // FP8 W0 row stride in bytes (K rounded up to 16)
+  int Kq = 0;         // MXFP4 W0 elements per row (K rounded up to 128)
   int nchild = 0;
   int fam[3] = {-1, -1, -1};
   int N[3] = {0, 0, 0};
@@ -97,8 +98,10 @@ struct Layout {
   uint32_t tied_mask = 0;
   GroupShape gs[WL_MAX_LAYER_TYPES][kGroups];
   std::vector<int64_t> w0;  // [(band * NT + tkey) * kGroups + g], -1 if absent
-  std::vector<int64_t> w0q; // FP8 bundles: per-row scales of that W0 block
+  std::vector<int64_t> w0q; // FP8: per-row scales of that W0 block; MXFP4: its block scales
   bool fp8 = false;
+  bool mxfp4 = false;
+  bool coded() const { return fp8 || mxfp4; }
   std::vector<LayerOff> lay;
   size_t bytes = 0;
   size_t zero_off = 0;  // 256 zero bytes
@@ -110,7 +113,11 @@ struct Layout {
   int64_t w0_at(int b, int t, int g) const { return w0[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
   int64_t &w0q_at(int b, int t, int g) { return w0q[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
   int64_t w0q_at(int b, int t, int g) const { return w0q[(static_cast<size_t>(b) * NT + t) * kGroups + g]; }
-  size_t w0_row_bytes(const GroupShape &gs) const { return fp8 ? static_cast<size_t>(gs.Kp) : static_cast<size_t>(gs.K) * 2; }
+  size_t w0_row_bytes(const GroupShape &gs) const {
+    return fp8 ? static_cast<size_t>(gs.Kp) : mxfp4 ? static_cast<size_t>(gs.Kq) / 2 : static_cast<size_t>(gs.K) * 2;
+  }
+  // bytes per row of the scale region after a coded W0 block
+  size_t w0_scale_row_bytes(const GroupShape &gs) const { return fp8 ? 4 : static_cast<size_t>(gs.Kq) / 32; }
 };
 
 bool tied(const Layout &lo, int t) { return (lo.tied_mask >> t) & 1u; }
@@ -123,9 +130,10 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
   if (G < 1 || G > L) return fail(WL_EINVAL, "num_bands %d must be in [1, num_layers=%d]", G, L);
   if (NT < 1 || NT > WL_MAX_LAYER_TYPES) return fail(WL_EINVAL, "num_layer_types %d must be 1 or 2", NT);
   if (spec->k_eq_v_type_mask >> NT) return fail(WL_EINVAL, "k_eq_v_type_mask 0x%x names a layer type >= %d", spec->k_eq_v_type_mask, NT);
-  if (spec->w0_format != WL_W0_BF16 && spec->w0_format != WL_W0_FP8)
+  if (spec->w0_format != WL_W0_BF16 && spec->w0_format != WL_W0_FP8 && spec->w0_format != WL_W0_MXFP4)
     return fail(WL_EINVAL, "w0_format %d invalid", spec->w0_format);
   lo.fp8 = spec->w0_format == WL_W0_FP8;
+  lo.mxfp4 = spec->w0_format == WL_W0_MXFP4;
   lo.L = L;
   lo.G = G;
   lo.NT = NT;
@@ -177,6 +185,7 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
         const int c = gs.nchild++;
         gs.K = K;
         gs.Kp = (K + 15) & ~15;
+        gs.Kq = (K + 127) & ~127;
         gs.fam[c] = f;
         gs.N[c] = N;
         gs.r[c] = spec->rank[t][f];
@@ -208,9 +217,9 @@ wl_status make_layout(const wl_bundle_spec *spec, Layout &lo) {
         const GroupShape &gs = lo.gs[t][g];
         lo.w0_at(b, t, g) = static_cast<int64_t>(off);
         off = align256(off + static_cast<size_t>(gs.Ntot) * lo.w0_row_bytes(gs));
-        if (lo.fp8) {
+        if (lo.coded()) {
           lo.w0q_at(b, t, g) = static_cast<int64_t>(off);
-          off = align256(off + static_cast<size_t>(gs.Ntot) * 4);
+          off = align256(off + static_cast<size_t>(gs.Ntot) * lo.w0_scale_row_bytes(gs));
         }
       }
     }
@@ -269,10 +278,10 @@ size_t ws_prefill_partial_bytes(const Layout &lo, int32_t T) {
   return align256(n);
 }
 
-// FP8 bundles: the bf16 expansion of the largest W0 row block a call reads
-// (prefill and materialization run the bf16 GEMM on it).
+// FP8 and MXFP4 bundles: the bf16 expansion of the largest W0 row block a
+// call reads (prefill and materialization run the bf16 GEMM on it).
 size_t ws_w0_expand_bytes(const Layout &lo) {
-  if (!lo.fp8) return 0;
+  if (!lo.coded()) return 0;
   size_t n = 0;
   for (int t = 0; t < lo.NT; ++t)
     for (int g = 0; g < kGroups; ++g) {
@@ -353,6 +362,12 @@ wl_status resolve(const wl_bundle *h, int32_t layer, int32_t family, int32_t sta
     c.W0f8 = A + w0off + static_cast<size_t>(rs0) * gs.Kp;
     c.q = reinterpret_cast<const float *>(A + lo.w0q_at(b, tkey, g)) + rs0;
     c.ldw0 = gs.Kp;
+  } else if (lo.mxfp4) {
+    c.W0 = nullptr;
+    c.ldw0 = gs.Kq / 2;
+    c.ldsc = gs.Kq / 32;
+    c.W0f4 = A + w0off + static_cast<size_t>(rs0) * c.ldw0;
+    c.sc4 = A + lo.w0q_at(b, tkey, g) + static_cast<size_t>(rs0) * c.ldsc;
   } else {
     c.W0 = reinterpret_cast<const uint16_t *>(A + w0off) + static_cast<size_t>(rs0) * gs.K;
   }
@@ -428,10 +443,11 @@ wl_status run_call(const wl_bundle *h, int32_t layer, int32_t family, int32_t st
     for (int c = 0; c < rv.c.nchild; ++c) rmax = std::max(rmax, static_cast<int>(rv.c.ch[c].rpad));
     if (wl::prefill_partial_bytes(rv.c.Ntot, rv.c.Rz, rmax, rv.c.K, T) > ws_prefill_partial_bytes(h->lo, T))
       return fail(WL_ENOSPACE, "internal: prefill partials of this call exceed the planned workspace");
-    if (h->lo.fp8) {
-      // FP8 bundle: expand this call's W0 rows to bf16 for the GEMM
+    if (h->lo.coded()) {
+      // FP8 / MXFP4 bundle: expand this call's W0 rows to bf16 for the GEMM
       uint16_t *w0 = reinterpret_cast<uint16_t *>(ws + ws_prefill_z_bytes(h->lo, T) + ws_prefill_partial_bytes(h->lo, T));
-      e = wl::launch_dequantize_rows(rv.c.W0f8, rv.c.ldw0, rv.c.q, rv.c.Ntot, rv.c.K, w0, s);
+      e = h->lo.fp8 ? wl::launch_dequantize_rows(rv.c.W0f8, rv.c.ldw0, rv.c.q, rv.c.Ntot, rv.c.K, w0, s)
+                    : wl::launch_dequantize_mxfp4(rv.c.W0f4, 2 * rv.c.ldw0, rv.c.sc4, rv.c.Ntot, rv.c.K, w0, s);
       if (e != hipSuccess) return hip_fail(e, "W0 expand launch");
       rv.c.W0 = w0;
     }
@@ -540,8 +556,8 @@ wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size
       return fail(WL_EINVAL, "source %zu (kind %d, index %d, type %d, family %d) is not part of this bundle", i, s.kind,
                   s.index, s.layer_type, s.family);
     if (it->second >= 0) return fail(WL_EINVAL, "source %zu duplicates source %d", i, it->second);
-    if (s.kind == WL_SRC_W0 && lo.fp8 && !s.on_device)
-      return fail(WL_EINVAL, "source %zu: an FP8 bundle codes W0 on the device; pass a device tensor", i);
+    if (s.kind == WL_SRC_W0 && lo.coded() && !s.on_device)
+      return fail(WL_EINVAL, "source %zu: an FP8 or MXFP4 bundle codes W0 on the device; pass a device tensor", i);
     it->second = static_cast<int>(i);
   }
   for (const auto &kv : expect)
@@ -566,6 +582,12 @@ wl_status theta_bundle_load(const wl_bundle_spec *spec, const wl_src *srcs, size
       if (lo.fp8) {
         float *q = reinterpret_cast<float *>(A + lo.w0q_at(s.index, t, g)) + gs.row_start[c];
         e = wl::launch_quantize_rows(static_cast<const uint16_t *>(s.ptr), gs.N[c], gs.K, dst, gs.Kp, q, strm);
+        if (e != hipSuccess) return hip_fail(e, "W0 quantize");
+        continue;
+      }
+      if (lo.mxfp4) {
+        uint8_t *sc = A + lo.w0q_at(s.index, t, g) + static_cast<size_t>(gs.row_start[c]) * lo.w0_scale_row_bytes(gs);
+        e = wl::launch_quantize_mxfp4(static_cast<const uint16_t *>(s.ptr), gs.N[c], gs.K, dst, gs.Kq, sc, strm);
         if (e != hipSuccess) return hip_fail(e, "W0 quantize");
         continue;
       }
@@ -700,9 +722,10 @@ wl_status weightless_materialize(const wl_bundle *bundle, int32_t layer, int32_t
   hipError_t e = wl::launch_transpose_v(c.Vt, ch.rpad, c.K, vrows, s);
   if (e != hipSuccess) return hip_fail(e, "transpose launch");
   const uint16_t *w0 = c.W0;
-  if (bundle->lo.fp8) {
+  if (bundle->lo.coded()) {
     uint16_t *buf = reinterpret_cast<uint16_t *>(static_cast<uint8_t *>(d_ws) + need - ws_w0_expand_bytes(bundle->lo));
-    e = wl::launch_dequantize_rows(c.W0f8, c.ldw0, c.q, c.Ntot, c.K, buf, s);
+    e = bundle->lo.fp8 ? wl::launch_dequantize_rows(c.W0f8, c.ldw0, c.q, c.Ntot, c.K, buf, s)
+                       : wl::launch_dequantize_mxfp4(c.W0f4, 2 * c.ldw0, c.sc4, c.Ntot, c.K, buf, s);
     if (e != hipSuccess) return hip_fail(e, "W0 expand launch");
     w0 = buf;
   }
