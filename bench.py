@@ -852,8 +852,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "prefill", "dense", "act", "fp8",
-                                                             "decompose", "small", "reuse"])
+    ap.add_argument("--only", default="all", choices=["all", "decode", "decode1", "decode2", "prefill", "dense", "act",
+                                                             "fp8", "decompose", "small", "reuse"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--band-reuse", action="store_true",
                     help="report whether a band-shared W0 re-read by the next layer is served from the 256 MB "
@@ -924,6 +924,7 @@ def main():
     if args.only in ("all", "decode"):
         res["decode4_t16"] = decode_section(wl4, 16, args.steps, args.warmup, dev)
         log(f"decode T=16: {res['decode4_t16']['GBps']:.1f} GB/s")
+    if args.only in ("all", "decode", "decode2"):
         res["decode2_t1"] = decode_section(synth.custom(26, 13, 32, dict(synth.workload(2).dims), cid=2),
                                            1, args.steps * 5, args.warmup, dev)
         log(f"gemma3 decode T=1: {res['decode2_t1']['GBps']:.1f} GB/s")

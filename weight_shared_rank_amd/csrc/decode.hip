@@ -55,7 +55,7 @@ namespace {
 #define WL_EPI_WAVES 2
 #endif
 #ifndef WL_DECODE_TARGET_WGS
-#define WL_DECODE_TARGET_WGS 4096
+#define WL_DECODE_TARGET_WGS 3072
 #endif
 #ifndef WL_STREAM_ROWS
 #define WL_STREAM_ROWS 2
@@ -798,7 +798,7 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
                        dim3(2 * kStreamWaves * 64), 0, stream, c, p_part, z_pair, nt_vt, KS);
   } else {
     KS = c.W0f8   ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV)
-         : c.W0f4 ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / kFp4KsDiv)
+         : c.W0f4 ? max(1, (decode_k_slices(c.Ntot, c.Rz, c.K) + kFp4KsDiv - 1) / kFp4KsDiv)
                   : decode_k_slices(c.Ntot, c.Rz, c.K);
     // with a coded W0 (FP8, MXFP4) the W0 workgroups stream a half or a
     // quarter of the bytes, and over a long K (>= kVtSplitK) a V^T tile over
