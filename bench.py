@@ -200,18 +200,20 @@ def source_sha(*names):
 
 
 def traffic_from_profile(key, sha):
-    """HBM bytes per call from the committed rocprofv3 counter summary
-    (profiles/counters.json), if it was taken on the current kernel source;
-    else None."""
+    """HBM bytes per call, read plus written, from the committed rocprofv3
+    counter summary (profiles/counters.json: calibrated FETCH_SIZE and
+    WRITE_SIZE), with the two parts, if it was taken on the current kernel
+    source; else (None, None, None)."""
     p = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(p):
-        return None
+        return None, None, None
     with open(p) as f:
         d = json.load(f)
     rec = d.get(key)
     if not rec or rec.get("source_sha") != sha:
-        return None
-    return rec.get("hbm_bytes_per_call")
+        return None, None, None
+    rd, wr = rec.get("hbm_bytes_per_call"), rec.get("hbm_write_bytes_per_call")
+    return (rd + wr if rd is not None and wr is not None else None), rd, wr
 
 
 def decode_section(wl, T, steps, warmup, dev, reps=3, w0_format="bf16"):
@@ -966,17 +968,20 @@ def main():
                                 "tokens": 1, "layers": 60, "bands": 5, "rank": 256,
                                 "bytes_read_per_step": d["bytes_read"], "hbm_frac": d["GBps"] / HBM_PEAK_GBS}})
         sha = source_sha("decode.hip", "common.h", "internal.h")
+        traffic, t_rd, t_wr = traffic_from_profile("decode", sha)
         line["roofline"] = {"bound": "hbm",
                             "kernel": "stream_kernel + epilogue_kernel (one decode call is these two launches; "
                                       "the stream launch moves ~95% of the bytes)",
                             "achieved": round(d["kernel_GBps"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(d["kernel_GBps"] / HBM_PEAK_GBS, 4),
                             "bytes_per_call": d["bytes_per_launch"], "avg_call_us": round(d["avg_launch_us"], 3),
-                            "traffic": traffic_from_profile("decode", sha), "source_sha": sha}
+                            "traffic": traffic, "traffic_read": t_rd, "traffic_written": t_wr,
+                            "source_sha": sha}
     line["detail"] = res
     if "prefill5" in res:
         p = res["prefill5"]
         psha = source_sha("prefill.hip", "common.h", "internal.h")
+        ptraffic, pt_rd, pt_wr = traffic_from_profile("prefill", psha)
         line["prefill"] = {"metric": "prefill TFLOP/s", "value": round(p["TFLOPs"], 2), "unit": "TFLOP/s",
                            "mfma_frac": round(p["mfma_frac"], 4), "peak": BF16_PEAK_TFLOPS,
                            "ms_per_step": round(p["step_s"] * 1e3, 3),
@@ -989,7 +994,8 @@ def main():
                                         "achieved": round(p["call_TFLOPs"], 2), "peak": BF16_PEAK_TFLOPS,
                                         "unit": "TFLOP/s", "frac": round(p["call_TFLOPs"] / BF16_PEAK_TFLOPS, 4),
                                         "flops_per_call": p["flops_per_call"], "avg_call_us": round(p["avg_call_us"], 2),
-                                        "traffic": traffic_from_profile("prefill", psha), "source_sha": psha}}
+                                        "traffic": ptraffic, "traffic_read": pt_rd, "traffic_written": pt_wr,
+                                        "source_sha": psha}}
         if "prefill3" in res:
             line["prefill"]["gemma3_1b_T2048_TFLOPs"] = round(res["prefill3"]["TFLOPs"], 2)
         if "prefill3_stacked" in res:
