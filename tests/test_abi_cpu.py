@@ -256,3 +256,20 @@ def test_decompose_workspace_and_argument_errors(L):
     assert call(omega=None) == -1
     assert call(ws=FAKE_ARENA + 16) == -1 and "aligned" in binding.last_error()
     assert call(wsb=1024) == -5
+
+
+def test_library_shares_torchs_hip_runtime(L):
+    """Loading the library before anything imports torch still leaves one HIP
+    runtime in the process (torch's): a second, system runtime beside it
+    would find no device.  Run in a fresh interpreter, binding first."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from weight_shared_rank_amd import binding\n"
+            "binding.lib()\n"
+            "import torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps), sorted(maps))\n" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split()[0] == "1", out.stdout

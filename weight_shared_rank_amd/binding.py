@@ -66,6 +66,11 @@ def lib():
         return _lib
     if not os.path.exists(LIBPATH):
         raise RuntimeError(f"{LIBPATH} is not built; run `python -m weight_shared_rank_amd.build`")
+    # torch's HIP runtime must be the process's only one: loaded first, it
+    # satisfies the library's libamdhip64 dependency.  Loaded the other way
+    # round, the library pulls in the system runtime beside torch's, and that
+    # second runtime finds no device.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIBPATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sig = {
