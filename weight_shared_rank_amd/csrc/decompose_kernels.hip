@@ -57,24 +57,31 @@ __global__ void scale_residual_kernel(const uint16_t *W, const uint16_t *W0, int
 }
 
 // C[M][N] = sum_k A(m, k) B(k, n), A(m, k) = A[m * sam + k * sak], B(k, n) =
-// B[k * sbk + n * sbn]; fp32, 64 x 64 tiles, 32 k per LDS tile, 256 threads
-// with 4 x 4 outputs each.  The next tile's elements are loaded into
-// registers while the current one is multiplied, so a workgroup pays the load
-// latency once per tile pair rather than once per tile; products are summed
-// in k order.  blockIdx.z takes the k range [z kc, (z+1) kc); with gridDim.z
-// > 1 each slice writes its own partial C_z at C + z M ldc and reduce_kernel
-// adds them in slice order (deterministic).  Tile loads walk the operand's
-// unit-stride index fastest (a_m_fast: sam == 1).
+// B[k * sbk + n * sbn]; fp32 on the matrix cores (v_mfma_f32_16x16x4_f32),
+// 64 x 64 tiles, 32 k per LDS tile, four waves each owning a 32 x 32 corner
+// (2 x 2 MFMA blocks).  The next tile's elements are loaded into registers
+// while the current one is multiplied, so a workgroup pays the load latency
+// once per tile pair rather than once per tile; products are summed in k
+// order, four k per MFMA.  blockIdx.z takes the k range [z kc, (z+1) kc);
+// with gridDim.z > 1 each slice writes its own partial C_z at C + z M ldc and
+// reduce_kernel adds them in slice order (deterministic).  Tile loads walk the
+// operand's unit-stride index fastest (a_m_fast: sam == 1).
 constexpr int kF32Kt = 32;
 __global__ void gemm_f32_kernel(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn,
                                 float *C, int64_t ldc, int M, int N, int K, int kc, int a_m_fast, int b_n_fast) {
   constexpr int EPT = kF32Kt * 64 / 256;  // elements of each operand per thread and tile
   __shared__ float As[kF32Kt][65], Bs[kF32Kt][65];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int mw = (wave >> 1) * 32, nw = (wave & 1) * 32;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int kbeg = blockIdx.z * kc, kend = min(K, kbeg + kc);
   C += static_cast<int64_t>(blockIdx.z) * M * ldc;
-  float acc[4][4] = {};
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ra[EPT], rb[EPT];
   auto load = [&](int k0) {
 #pragma unroll
@@ -101,29 +108,33 @@ __global__ void gemm_f32_kernel(const float *A, int64_t sam, int64_t sak, const 
     __syncthreads();
     if (k0 + kF32Kt < kend) load(k0 + kF32Kt);  // in flight during the products below
 #pragma unroll
-    for (int kk = 0; kk < kF32Kt; ++kk) {
-      float a[4], b[4];
+    for (int k4 = 0; k4 < kF32Kt; k4 += 4) {
+      // A block rows i: lane holds A(mw + 16 i + r16, k4 + g); B columns j: B(k4 + g, nw + 16 j + r16)
+      float a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+      for (int i = 0; i < 2; ++i) a[i] = As[k4 + g][mw + 16 * i + r16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+      for (int j = 0; j < 2; ++j) b[j] = Bs[k4 + g][nw + 16 * j + r16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
+  // lane holds C(mw + 16 i + 4 g + e, nw + 16 j + r16)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gm = m0 + ty * 4 + i;
-    if (gm >= M) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + tx * 4 + j;
-      if (gn < N) C[gm * ldc + gn] = acc[i][j];
+    for (int e = 0; e < 4; ++e) {
+      const int gm = m0 + mw + 16 * i + 4 * g + e;
+      if (gm >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int gn = n0 + nw + 16 * j + r16;
+        if (gn < N) C[gm * ldc + gn] = acc[i][j][e];
+      }
     }
-  }
 }
 
 // C[m][n] = sum over z = 0 .. splits-1, in order, of P[z][m][n] (P dense

@@ -49,6 +49,7 @@
 // zero row; B = the child's columns of Z), so U z is added at MFMA rate
 // before y is rounded to bf16 and stored.
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "internal.h"
@@ -899,17 +900,28 @@ __global__ void finish_kernel(FinishArgs a) {
   }
 }
 
+// Raise a kernel's dynamic-LDS limit to what its ring needs, once per kernel
+// and device (the attribute belongs to the device the call runs on).
+template <auto KERN>
+hipError_t ensure_lds(size_t bytes) {
+  static std::atomic<uint64_t> done{0};  // bit d: set on device d (d < 64)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(KERN), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(bytes));
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
 template <int BM, int BN, int WM, int WN, int NST, bool PAIRED>
 hipError_t launch_gemm_inst(const GemmArgs &a, hipStream_t stream) {
   using TL = Tile<BM, BN, WM, WN, NST>;
   auto kern = gemm_kernel<BM, BN, WM, WN, NST, PAIRED>;
-  static bool attr_set = false;  // per instance; setting it twice is harmless
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(TL::LDS));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = ensure_lds<gemm_kernel<BM, BN, WM, WN, NST, PAIRED>>(TL::LDS);
+  if (e != hipSuccess) return e;
   const int units = a.nM * a.nT * (a.mode == kPartial ? a.ksplit : 1);
   hipLaunchKernelGGL(kern, dim3(units), dim3(WM * WN * 64), TL::LDS, stream, a);
   return hipGetLastError();
@@ -1036,13 +1048,8 @@ template <int BM, int BN, int WM, int WN, int NST, int RZ>
 hipError_t launch_fz_inst(const GemmArgs &a, hipStream_t stream) {
   using TL = Tile<BM, BN, WM, WN, NST, RZ>;
   auto kern = gemm_fz_kernel<BM, BN, WM, WN, NST, RZ>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(TL::LDS));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = ensure_lds<gemm_fz_kernel<BM, BN, WM, WN, NST, RZ>>(TL::LDS);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(a.nM * a.nT), dim3(WM * WN * 64), TL::LDS, stream, a);
   return hipGetLastError();
 }
