@@ -665,7 +665,7 @@ __device__ __forceinline__ void store_fused_tile(const f32x4 (&acc)[BM / WM / 16
 // every feature tile of its column: RZ / BM more MFMA work, traded for the
 // two launches (the Z product and its sum) it saves.
 template <int BM, int BN, int WM, int WN, int NST, int RZ>
-__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_fz_kernel(GemmArgs a) {
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN > 8 ? WM * WN / 4 : 1, WM * WN > 8 ? WM * WN / 4 : 2))) void gemm_fz_kernel(GemmArgs a) {
   using TL = Tile<BM, BN, WM, WN, NST, RZ>;
   static_assert(RZ % 64 == 0, "Z rows are whole 64-rank blocks (the chunk swizzle stays inside a row)");
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -935,9 +935,10 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
 
 // Tile shapes: BM features x BN tokens.  eff ranks the shapes by measured
 // streaming efficiency (bigger tiles move fewer bytes per flop).  Every
-// shape runs on eight waves: a CU's LDS-DMA rate grows with the waves
-// issuing loads, so the small tiles, which hold one workgroup per CU for
-// their ring, keep eight waves loading rather than four.
+// shape runs on at least eight waves: a CU's LDS-DMA rate grows with the
+// waves issuing loads, so the small tiles, which hold one workgroup per CU
+// for their ring, keep eight (the fused-Z 128 x 64 tile sixteen) waves
+// loading rather than four.
 struct TileCfg {
   int BM, BN;
   double eff;
@@ -1071,7 +1072,7 @@ hipError_t launch_fused_z(GemmArgs a, const Plan &p, int RZ, hipStream_t stream)
       // deeper ring of one workgroup per CU is faster.
       if (r64 && static_cast<long>(p.nM) * p.nT >= 2L * kCUs) return launch_fz_inst<128, 128, 4, 2, 2, 64>(a, stream);
       return r64 ? launch_fz_inst<128, 128, 4, 2, 3, 64>(a, stream) : launch_fz_inst<128, 128, 4, 2, 3, 128>(a, stream);
-    case 1: return r64 ? launch_fz_inst<128, 64, 2, 4, 4, 64>(a, stream) : launch_fz_inst<128, 64, 2, 4, 3, 128>(a, stream);
+    case 1: return r64 ? launch_fz_inst<128, 64, 4, 4, 4, 64>(a, stream) : launch_fz_inst<128, 64, 2, 4, 3, 128>(a, stream);
     default: return r64 ? launch_fz_inst<64, 64, 4, 2, 4, 64>(a, stream) : launch_fz_inst<64, 64, 4, 2, 4, 128>(a, stream);
   }
 }
