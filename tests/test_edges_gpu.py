@@ -360,3 +360,23 @@ def test_four_row_tiles_many_tokens(four_tile_bundle, T):
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), c
         res = compare(np64(y), ow.call(0, c, np64(x)))
         assert res["ok"], f"{c} T={T}: {res}"
+
+
+@pytest.mark.parametrize("fam,N", [("gate", 4100), ("k", 264)])
+def test_fused_z_ragged_large_calls(gpu_lib, fam, N):
+    """Small-rank prefill calls with ragged rows, tokens and K (a K tail of 8):
+    the gate-shaped call has 33 x 17 = 561 tiles of 128 x 128, enough for the
+    fused-Z tile that runs two workgroups per CU; the k-shaped call takes the
+    128 x 64 fused-Z tile with partial row and token tiles."""
+    wl = synth.custom(1, 1, 40, {(0, fam): (N, 1160)}, cid=95)
+    ow = OracleWorkload(wl, DEV)
+    b = sdev.load(wl, DEV)
+    x = wl.x(0, fam, 2050, DEV)
+    announce(f"fused-Z ragged {fam} N={N} T=2050")
+    y = b.linear(0, fam, x)
+    torch.cuda.synchronize()
+    res = compare(np64(y), ow.call(0, fam, np64(x)))
+    assert res["ok"], res
+    y2 = b.linear(0, fam, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
