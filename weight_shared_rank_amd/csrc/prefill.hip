@@ -12,16 +12,16 @@
 // GEMM core (gfx950).  A workgroup owns a BM x BN output tile: BM weight rows
 // ("features", MFMA A operand) by BN tokens (B operand).  Both operands are
 // K-contiguous rows.  Stages of 64 k (128 bytes per row) move global -> LDS by
-// global_load_lds_dwordx4 (no VGPR staging) into an NST-stage ring.  One wave
-// instruction fills 8 rows x 128 bytes: lane i writes LDS slot i % 8 of row
+// buffer_load_dwordx4 ... lds (no VGPR staging) into an NST-stage ring.  One
+// wave instruction fills 8 rows x 128 bytes: lane i writes LDS slot i % 8 of row
 // i / 8 and fetches 16-byte chunk c = (i % 8) ^ (row % 8) of that row, so
 // chunk c of row r sits in slot c ^ (r % 8).  A 16-byte fragment read (8
 // lanes per LDS phase: 8 consecutive rows, one chunk) then touches 8
 // different slots, i.e. all 32 banks once.  Whole 128-byte rows per request
 // halve the per-CU request count of 64-byte rows, and the request rate per CU,
 // not the MFMA rate, is what bounds the operand stream at a few hundred
-// tokens.  Lanes whose row or k lies outside the operand fetch a row of zeros
-// kept in the arena (an LDS-DMA lane cannot be zero-filled).
+// tokens.  Lanes whose row or k lies outside the operand take an offset past
+// the load's buffer range, which the buffer unit returns as zeros.
 //
 // Scheduling.  Workgroups are numbered XCD-major: hardware assigns workgroup
 // w to XCD w % 8, and the unit order is remapped so that each XCD walks a
@@ -45,8 +45,8 @@
 //
 // Epilogue of the main GEMM: the fp32 accumulators are scaled by s per
 // feature row, then the same staged loop runs over the ranks of every child
-// whose rows meet the tile (A = that child's U rows, other rows read the
-// zero row; B = the child's columns of Z), so U z is added at MFMA rate
+// whose rows meet the tile (A = that child's U rows, other rows read
+// zeros; B = the child's columns of Z), so U z is added at MFMA rate
 // before y is rounded to bf16 and stored.
 #include <algorithm>
 #include <atomic>
@@ -71,6 +71,47 @@ constexpr double kStepFloor = 0.55;
 constexpr double kSplitLaunch = 4.0;
 constexpr int kMaxSplit = 16;
 constexpr int kCUs = 256;
+
+// LDS-DMA stage loads.  They are buffer loads into LDS (buffer_load_dwordx4
+// ... lds), not global_load_lds: with the latter in flight the compiler
+// drains every outstanding LDS read (s_waitcnt lgkmcnt(0)) before each use of
+// a fragment, with the former it counts them (lgkmcnt(n)), so fragment reads
+// stay in flight under the MFMAs (same results; the 31B prefill GEMMs ran
+// 2-7% faster).  One load instruction of a wave (8 rows x 128 bytes) reads
+// through one descriptor whose base is its first live lane's address less
+// 128 bytes; each lane adds a 32-bit byte offset.  The rows of one
+// instruction ascend with the lane (every caller maps lane >> 3 to
+// consecutive rows of one operand), so every live offset is positive and
+// small.  A lane without a row takes an offset past the descriptor's range,
+// which the buffer unit returns as zeros.
+constexpr int kBufWord3 = 0x00020000;          // raw gfx9 descriptor: no swizzle, stride 0
+constexpr int kBufRange = 0x40000000;          // bytes the offsets are checked against
+constexpr uint32_t kBufNoRow = 0x7ffffff0u;    // past the range: reads zeros
+
+struct RowLoad {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off;  // this lane's byte offset (kBufNoRow: no row)
+};
+
+// p: this lane's source address, or null for no row; fallback: any valid
+// address, the base when no lane of the wave has a row.
+__device__ __forceinline__ RowLoad row_load(const uint16_t *p, const uint16_t *fallback) {
+  const uint64_t live = __builtin_amdgcn_ballot_w64(p != nullptr);
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(p);
+  uintptr_t base = reinterpret_cast<uintptr_t>(fallback);
+  if (live) {
+    const int first = __builtin_ctzll(live);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(addr), first);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(addr >> 32), first);
+    base = ((static_cast<uintptr_t>(hi) << 32) | lo) - kRowBytes;
+  }
+  return RowLoad{__builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), 0, kBufRange, kBufWord3),
+                 p != nullptr ? static_cast<uint32_t>(addr - base) : kBufNoRow};
+}
+
+__device__ __forceinline__ void load_rows(const RowLoad &r, uint32_t off, uint8_t *dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.rsrc, (lds_void *)dst, 16, off, 0, 0, 0);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -140,8 +181,8 @@ struct Tile {
 
 // One staged GEMM segment: acc += A B^T over 64-k steps [s_begin, s_end).
 // Row pointers are per load instruction (already offset to the lane's chunk);
-// a null row pointer reads the zero row.  klen bounds the valid k (chunks at
-// or past klen read the zero row).  With RZ > 0 the A rows BM .. BM+RZ-1 are
+// a null row pointer reads zeros.  klen bounds the valid k (chunks at or past
+// klen read zeros).  With RZ > 0 the A rows BM .. BM+RZ-1 are
 // V^T rows whose products go to zacc.
 template <int BM, int BN, int WM, int WN, int NST, int RZ>
 __device__ __forceinline__ void segment_rz(f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
@@ -160,16 +201,16 @@ __device__ __forceinline__ void segment_rz(f32x4 (&acc)[BM / WM / 16][BN / WN / 
     const int gq = wave * TL::LPW + q;
     ldsoff[q] = gq < TL::GA ? gq * 1024 : TL::AR * kRowBytes + (gq - TL::GA) * 1024;
   }
-  // Running source pointers, one per load instruction, advanced by one stage
-  // per issue (stages are issued in order); a lane without a row reads the
-  // zero row and never advances.  Only a last step that reaches past klen
-  // (K not a multiple of 64) needs the per-chunk bound.
-  const uint16_t *cur[TL::LPW];
-  int inc[TL::LPW];
+  // Running source offsets, one per load instruction, advanced by one stage
+  // per issue (stages are issued in order); a lane without a row reads zeros
+  // and never advances.  Only a last step that reaches past klen (K not a
+  // multiple of 64) needs the per-chunk bound.
+  RowLoad src[TL::LPW];
+  uint32_t inc[TL::LPW];
 #pragma unroll
   for (int q = 0; q < TL::LPW; ++q) {
-    inc[q] = rp[q] != nullptr ? kBK : 0;
-    cur[q] = rp[q] != nullptr ? rp[q] + s_begin * kBK : zero_row;
+    src[q] = row_load(rp[q] != nullptr ? rp[q] + s_begin * kBK : nullptr, zero_row);
+    inc[q] = rp[q] != nullptr ? kRowBytes : 0;
   }
   const int full_steps = klen / kBK;
   // loads q0 .. q1-1 of a stage
@@ -179,10 +220,8 @@ __device__ __forceinline__ void segment_rz(f32x4 (&acc)[BM / WM / 16][BN / WN / 
 #pragma unroll
     for (int q = 0; q < TL::LPW; ++q) {
       if (q < q0 || q >= q1) continue;
-      const uint16_t *src = (tail && k >= klen) ? zero_row : cur[q];
-      __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
-                                       (lds_void *)(lds + stage * TL::STAGE + ldsoff[q]), 16, 0, 0);
-      cur[q] += inc[q];
+      load_rows(src[q], (tail && k >= klen) ? kBufNoRow : src[q].off, lds + stage * TL::STAGE + ldsoff[q]);
+      src[q].off += inc[q];
     }
   };
   auto issue = [&](int stage, int step) { issue_part(stage, step, 0, TL::LPW); };
@@ -258,7 +297,7 @@ __device__ __forceinline__ void segment(f32x4 (&acc)[BM / WM / 16][BN / WN / 16]
 // multiplies only its own child's rows, where two separate segments would
 // each run half the tile on zero rows.  Two 64-k stages of BM + 2 BN rows in
 // the ring (which has room for them for every tile shape).  Rank steps past
-// a child's padded rank read the zero row.
+// a child's padded rank read zeros.
 template <int BM, int BN, int WM, int WN, int NST>
 __device__ __forceinline__ void paired_delta(f32x4 (&acc)[BM / WM / 16][BN / WN / 16], const GemmArgs &a, int f,
                                              int n0, uint8_t *lds) {
@@ -277,6 +316,7 @@ __device__ __forceinline__ void paired_delta(f32x4 (&acc)[BM / WM / 16][BN / WN 
   const int nsteps = (max(cg.rpad, cu.rpad) + kBK - 1) / kBK;
   const uint16_t *rp[LPW2];
   int klen[LPW2], ldsoff[LPW2];
+  RowLoad src[LPW2];
 #pragma unroll
   for (int q = 0; q < LPW2; ++q) {
     const int gq = wave * LPW2 + q;
@@ -297,14 +337,14 @@ __device__ __forceinline__ void paired_delta(f32x4 (&acc)[BM / WM / 16][BN / WN 
       ldsoff[q] = BM * kRowBytes + gb * 1024;
     }
   }
+#pragma unroll
+  for (int q = 0; q < LPW2; ++q) src[q] = row_load(rp[q], a.zero_row);
   auto issue = [&](int stage, int step) __attribute__((always_inline)) {
     const int k = step * kBK + lchunk * 8;
 #pragma unroll
-    for (int q = 0; q < LPW2; ++q) {
-      const uint16_t *src = (rp[q] != nullptr && k < klen[q]) ? rp[q] + step * kBK : a.zero_row;
-      __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
-                                       (lds_void *)(lds + stage * STAGE2 + ldsoff[q]), 16, 0, 0);
-    }
+    for (int q = 0; q < LPW2; ++q)
+      load_rows(src[q], (rp[q] != nullptr && k < klen[q]) ? src[q].off + step * kRowBytes : kBufNoRow,
+                lds + stage * STAGE2 + ldsoff[q]);
   };
   const int arow = (wm * TL::TM + r16) * kRowBytes;
   const int region = wm * TL::TM < HB ? 0 : 1;  // gate waves read Z_gate, up waves Z_up
@@ -654,13 +694,13 @@ __device__ __forceinline__ void store_fused_tile(const f32x4 (&acc)[BM / WM / 16
 // One launch for a whole call with a small total rank (Rz <= RZ, RZ 64 or
 // 128): the workgroup of a BM x BN tile also computes its tokens' Z = X V.
 // Every stage of the main loop holds, after the BM rows of W0, the RZ rows
-// of V^T (rows past Rz read the zero row), so the X rows already staged for
+// of V^T (rows past Rz read zeros), so the X rows already staged for
 // the main product serve the thin reduction too; the waves accumulate
 // W0 x and V^T x side by side.  Then Z is rounded to bf16 (as between the
 // two launches of the unfused path) into LDS, token-major with 16-byte
 // chunk c of token t at slot c ^ (t % 8), the main accumulator is scaled by
 // s, and each child's U rows (A, streamed 64 ranks per step; ranks past the
-// child's padded rank read the zero row) multiply its columns of Z (B, from
+// child's padded rank read zeros) multiply its columns of Z (B, from
 // LDS) into it before the bf16 store.  Each token tile's Z is recomputed by
 // every feature tile of its column: RZ / BM more MFMA work, traded for the
 // two launches (the Z product and its sum) it saves.
@@ -745,15 +785,19 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WM 
   for (int ci = 0; ci < a.nchild; ++ci) {
     const ChildDesc &ch = a.ch[ci];
     if (ch.rpad == 0 || f * BM >= ch.row_start + ch.N || f * BM + BM <= ch.row_start) continue;
+    RowLoad usrc[LPU];
+#pragma unroll
+    for (int q = 0; q < LPU; ++q) {
+      const int row = f * BM + (wave * LPU + q) * 8 + lrow;
+      const bool in = row < a.M && row >= ch.row_start && row < ch.row_start + ch.N;
+      usrc[q] = row_load(in ? ch.U + static_cast<int64_t>(row - ch.row_start) * ch.rpad + lchunk * 8 : nullptr,
+                         a.zero_row);
+    }
     for (int st = 0; st * kBK < ch.rpad; ++st) {
 #pragma unroll
       for (int q = 0; q < LPU; ++q) {
-        const int gq = wave * LPU + q;
-        const int row = f * BM + gq * 8 + lrow;
         const int k = st * kBK + lchunk * 8;
-        const bool in = row < a.M && row >= ch.row_start && row < ch.row_start + ch.N && k < ch.rpad;
-        const uint16_t *src = in ? ch.U + static_cast<int64_t>(row - ch.row_start) * ch.rpad + k : a.zero_row;
-        __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void *)(ubuf + gq * 1024), 16, 0, 0);
+        load_rows(usrc[q], k < ch.rpad ? usrc[q].off + st * kRowBytes : kBufNoRow, ubuf + (wave * LPU + q) * 1024);
       }
       wait_vmcnt<0>();
       __syncthreads();
