@@ -960,9 +960,24 @@ hipError_t ensure_lds(size_t bytes) {
   return e;
 }
 
+// The stage loads address 8 rows of an operand from one buffer descriptor:
+// the offsets of a load instruction must stay inside its range over the
+// whole K (8 row strides plus the row length, in bytes).  Far beyond any
+// model shape; checked so that a larger stride fails rather than reads zeros.
+bool buffer_offsets_fit(const GemmArgs &a) {
+  int64_t ld = std::max<int64_t>({a.lda, a.ldb, a.ldz, a.ldv});
+  int64_t len = a.K;
+  for (int i = 0; i < a.nchild; ++i) {
+    ld = std::max<int64_t>(ld, a.ch[i].rpad);
+    len = std::max<int64_t>(len, a.ch[i].rpad);
+  }
+  return 2 * (8 * ld + len) + 2 * kRowBytes <= kBufRange;
+}
+
 template <int BM, int BN, int WM, int WN, int NST, bool PAIRED>
 hipError_t launch_gemm_inst(const GemmArgs &a, hipStream_t stream) {
   using TL = Tile<BM, BN, WM, WN, NST>;
+  if (!buffer_offsets_fit(a)) return hipErrorInvalidValue;
   auto kern = gemm_kernel<BM, BN, WM, WN, NST, PAIRED>;
   const hipError_t e = ensure_lds<gemm_kernel<BM, BN, WM, WN, NST, PAIRED>>(TL::LDS);
   if (e != hipSuccess) return e;
@@ -1095,6 +1110,7 @@ Plan plan_fused_z(int M, int K, int T, int RZ, int dsteps) {
 template <int BM, int BN, int WM, int WN, int NST, int RZ>
 hipError_t launch_fz_inst(const GemmArgs &a, hipStream_t stream) {
   using TL = Tile<BM, BN, WM, WN, NST, RZ>;
+  if (!buffer_offsets_fit(a)) return hipErrorInvalidValue;
   auto kern = gemm_fz_kernel<BM, BN, WM, WN, NST, RZ>;
   const hipError_t e = ensure_lds<gemm_fz_kernel<BM, BN, WM, WN, NST, RZ>>(TL::LDS);
   if (e != hipSuccess) return e;
