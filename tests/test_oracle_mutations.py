@@ -101,6 +101,61 @@ def test_decompose_mutants_are_caught(monkeypatch, name, attr, mutant):
     assert caught >= 1, f"{name} passed every decomposition pin"
 
 
+def _mean_shared_block(weights, scales, deltas, W0_prev):
+    # ignores the scales: the plain mean of W_l - D_l
+    return sum(np.asarray(W, np.float64) - D for W, D in zip(weights, deltas)) / len(weights)
+
+
+def _sum_s_shared_block(weights, scales, deltas, W0_prev):
+    # divides by sum s instead of sum s^2
+    num = sum(np.asarray(s)[:, None] * (np.asarray(W, np.float64) - D) for W, s, D in zip(weights, scales, deltas))
+    den = sum(np.asarray(s) for s in scales)
+    return num / np.where(den == 0, 1.0, den)[:, None]
+
+
+def _als_with(slip):
+    """als_band with one slip in its per-layer steps."""
+    def als(weights, rank, sweeps, store=True):
+        W0, members = decompose.decompose_band(weights, rank, store)
+        Ws = [np.asarray(W, np.float64) for W in weights]
+        for _ in range(sweeps):
+            deltas = [decompose.delta_product(m["U"], m["V"]) for m in members]
+            W0 = decompose.shared_block_given(Ws, [m["s"] for m in members], deltas, W0)
+            new = []
+            for W, D in zip(Ws, deltas):
+                s = decompose.row_scale(W if slip == "s ignores delta" else W - D, W0)
+                R = decompose.residual(W, W0, s)
+                if slip == "delta subtracted twice":
+                    R = R - D
+                U, V, S = decompose.truncated_factors(R, rank)
+                new.append({"s": s, "U": U, "V": V, "sigma": S,
+                            "err": decompose.rel_frobenius_error(W, W0, s, U, V)})
+            members = new
+        return W0, members
+    return als
+
+
+@pytest.mark.parametrize("name,attr,mutant", [
+    ("W0 step ignores the scales", "shared_block_given", _mean_shared_block),
+    ("W0 step divides by sum s", "shared_block_given", _sum_s_shared_block),
+    ("s step ignores the delta", "als_band", _als_with("s ignores delta")),
+    ("delta fitted to the residual less the old delta", "als_band", _als_with("delta subtracted twice")),
+])
+def test_als_mutants_are_caught(monkeypatch, name, attr, mutant):
+    monkeypatch.setattr(decompose, attr, mutant)
+    caught = 0
+    for pin, args in [(pins.test_als_objective_never_increases, (3, 10, 7, 2)),
+                      (pins.test_als_objective_never_increases, (5, 12, 12, 3)),
+                      (pins.test_als_shared_block_is_least_squares, ()),
+                      (pins.test_als_scale_step_is_stationary, ()),
+                      (pins.test_als_single_layer_band_stays_exact, ())]:
+        try:
+            pin(*args)
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"{name} passed every ALS pin"
+
+
 _orig_activation = forward.activation
 
 
