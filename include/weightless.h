@@ -287,6 +287,29 @@ wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K,
                                int32_t power_iters, const float *d_omega, void *d_w0, float *d_s, void *d_u,
                                void *d_v, void *d_ws, size_t ws_bytes, void *stream);
 
+/* ---- ALS refinement of the decomposition ("Quality (Gemma 4 31B)" page,
+ * "ALS optimization barely helps": alternating least squares, tried there as
+ * an improvement over the mean W0; the page gives no steps) ----
+ * weightless_decompose, then `sweeps` sweeps of block-coordinate least
+ * squares on J = sum_l ||W_l - diag(s_l) W0 - U_l V_l^T||_F^2, each sweep:
+ *   1. W0 = bf16(sum_l s_l (.) (W_l - U_l V_l^T) / sum_l s_l^2), row by row
+ *      (fp32 sums in layer order; a row whose scales are all zero keeps W0);
+ *   2. per layer, s_i = <(W - U V^T)_i, W0_i> / <W0_i, W0_i> in fp64 (1 for a
+ *      zero W0 row), stored fp32;
+ *   3. per layer, U V^T = the rank-r randomized truncated SVD of
+ *      W - diag(s) W0, as in weightless_decompose (same d_omega).
+ * U V^T in steps 1 and 2 is formed in fp32 from the stored bf16 U and V.
+ * Each step minimizes J over its block (the SVD up to the sketch's accuracy),
+ * so J does not grow from sweep to sweep beyond the rounding and the sketch
+ * error.  sweeps == 0 gives weightless_decompose's outputs bit for bit.
+ * Arguments, layouts and errors as weightless_decompose, plus: sweeps in
+ * [0, 64] (WL_EINVAL otherwise); d_ws >= weightless_decompose_als_workspace_bytes
+ * (N, K, rank, oversample) bytes (adds N x K + N fp32 sums). */
+size_t weightless_decompose_als_workspace_bytes(int32_t N, int32_t K, int32_t rank, int32_t oversample);
+wl_status weightless_decompose_als(const void *d_w, int32_t m, int32_t N, int32_t K, int32_t rank, int32_t oversample,
+                                   int32_t power_iters, int32_t sweeps, const float *d_omega, void *d_w0, float *d_s,
+                                   void *d_u, void *d_v, void *d_ws, size_t ws_bytes, void *stream);
+
 /* Output width N of a single-family call, or of a stacked call (stack >= 0
  * with family < 0); 0 on error.  Host-only. */
 int32_t weightless_out_dim(const wl_bundle *bundle, int32_t layer, int32_t family, int32_t stack);

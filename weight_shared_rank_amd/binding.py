@@ -33,7 +33,8 @@ EXPORTS = ("theta_bundle_arena_bytes", "theta_bundle_load", "theta_bundle_free",
            "weightless_workspace_bytes",
            "weightless_linear", "weightless_linear_noalloc", "weightless_stacked_linear", "weightless_out_dim", "wl_last_error",
            "weightless_materialize_workspace_bytes", "weightless_materialize", "weightless_gate_up_act",
-           "weightless_decompose_workspace_bytes", "weightless_decompose")
+           "weightless_decompose_workspace_bytes", "weightless_decompose",
+           "weightless_decompose_als_workspace_bytes", "weightless_decompose_als")
 
 
 class WlBundleSpec(ctypes.Structure):
@@ -89,6 +90,8 @@ def lib():
         "weightless_gate_up_act": (i32, [vp, i32, i32, vp, i32, vp, vp, sz, vp]),
         "weightless_decompose_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "weightless_decompose": (i32, [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "weightless_decompose_als_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "weightless_decompose_als": (i32, [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -289,13 +292,16 @@ def sketch_columns(N: int, K: int, rank: int, oversample: int) -> int:
     return min(rank + oversample, N, K)
 
 
-def decompose(w, rank: int, omega=None, oversample: int = 16, power_iters: int = 4, stream=None):
+def decompose(w, rank: int, omega=None, oversample: int = 16, power_iters: int = 4, stream=None,
+              als_sweeps: int = None):
     """Decompose one band of one family on the GPU.
 
     w: bf16 [m, N, K] device tensor (the band's layers in layer order);
     omega: fp32 [K, l] device test matrix, l = sketch_columns(N, K, rank, oversample)
-    (required when rank > 0).  Returns (W0 bf16 [N, K], s fp32 [m, N],
-    U bf16 [m, N, rank], V bf16 [m, K, rank]), the layouts theta_bundle_load takes."""
+    (required when rank > 0).  als_sweeps: None calls weightless_decompose;
+    an integer calls weightless_decompose_als with that many ALS sweeps.
+    Returns (W0 bf16 [N, K], s fp32 [m, N], U bf16 [m, N, rank], V bf16
+    [m, K, rank]), the layouts theta_bundle_load takes."""
     import torch
     if w.dim() != 3 or w.dtype != torch.bfloat16 or not w.is_cuda or not w.is_contiguous():
         raise WlError(-1, "w must be a contiguous bf16 [m, N, K] device tensor")
@@ -306,16 +312,19 @@ def decompose(w, rank: int, omega=None, oversample: int = 16, power_iters: int =
         if omega is None or tuple(omega.shape) != (k, l) or omega.dtype != torch.float32 \
                 or not omega.is_contiguous() or omega.device != dev:
             raise WlError(-1, f"omega must be a contiguous fp32 [{k}, {l}] tensor on {dev}")
-    need = lib().weightless_decompose_workspace_bytes(n, k, rank, oversample)
+    als = als_sweeps is not None
+    need = (lib().weightless_decompose_als_workspace_bytes if als else lib().weightless_decompose_workspace_bytes)(
+        n, k, rank, oversample)
     if need == 0:
-        raise WlError(-1, "weightless_decompose_workspace_bytes: arguments out of range")
+        raise WlError(-1, "decomposition workspace size: arguments out of range")
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     w0 = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
     s = torch.empty((m, n), dtype=torch.float32, device=dev)
     u = torch.empty((m, n, rank), dtype=torch.bfloat16, device=dev)
     v = torch.empty((m, k, rank), dtype=torch.bfloat16, device=dev)
-    _check(lib().weightless_decompose(w.data_ptr(), m, n, k, rank, oversample, power_iters,
-                                      omega.data_ptr() if rank > 0 else None, w0.data_ptr(), s.data_ptr(),
-                                      u.data_ptr() if rank > 0 else None, v.data_ptr() if rank > 0 else None,
-                                      ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
+    lead = (w.data_ptr(), m, n, k, rank, oversample, power_iters) + ((als_sweeps,) if als else ())
+    fn = lib().weightless_decompose_als if als else lib().weightless_decompose
+    _check(fn(*lead, omega.data_ptr() if rank > 0 else None, w0.data_ptr(), s.data_ptr(),
+              u.data_ptr() if rank > 0 else None, v.data_ptr() if rank > 0 else None,
+              ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
     return w0, s, u, v

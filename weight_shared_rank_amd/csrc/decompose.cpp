@@ -184,11 +184,7 @@ wl_status report(wl_status st, const char *what, int layer, hipError_t e) {
   return st;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t weightless_decompose_workspace_bytes(int32_t N, int32_t K, int32_t rank, int32_t oversample) {
+size_t base_workspace_bytes(int32_t N, int32_t K, int32_t rank, int32_t oversample) {
   if (N <= 0 || K <= 0 || rank < 0 || oversample < 0) return 0;
   const size_t l = static_cast<size_t>(std::min<int64_t>(static_cast<int64_t>(rank) + oversample, std::min(N, K)));
   size_t n = align256(static_cast<size_t>(N) * K * 4);        // R
@@ -202,17 +198,28 @@ size_t weightless_decompose_workspace_bytes(int32_t N, int32_t K, int32_t rank, 
   return n;
 }
 
-wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K, int32_t rank, int32_t oversample,
-                               int32_t power_iters, const float *d_omega, void *d_w0, float *d_s, void *d_u,
-                               void *d_v, void *d_ws, size_t ws_bytes, void *stream) {
+// The ALS shared-block step's sums: num (fp32 [N][K]) and den (fp32 [N]).
+size_t als_extra_bytes(int32_t N, int32_t K) {
+  return align256(static_cast<size_t>(N) * K * 4) + align256(static_cast<size_t>(N) * 4);
+}
+
+// The one-shot decomposition of a band, then `sweeps` ALS sweeps: the shared
+// block refit from every layer's s and U V^T (fp32 sums in layer order,
+// rounded to bf16), then per layer the scale against W0 with the current
+// delta removed and the truncated SVD of the new residual, as in the one-shot
+// pass.  The deltas are recomputed in fp32 from the stored bf16 U and V.
+wl_status decompose_band(const void *d_w, int32_t m, int32_t N, int32_t K, int32_t rank, int32_t oversample,
+                         int32_t power_iters, int32_t sweeps, const float *d_omega, void *d_w0, float *d_s,
+                         void *d_u, void *d_v, void *d_ws, size_t ws_bytes, void *stream) {
   if (m < 1 || N < 1 || K < 1 || rank < 0 || oversample < 0 || power_iters < 0 || power_iters > 16)
     return report(WL_EINVAL, "need m, N, K >= 1, rank, oversample >= 0 and 0 <= power_iters <= 16", -1, hipSuccess);
+  if (sweeps < 0 || sweeps > 64) return report(WL_EINVAL, "need 0 <= sweeps <= 64", -1, hipSuccess);
   if (rank > std::min(N, K)) return report(WL_ESHAPE, "rank exceeds min(N, K)", -1, hipSuccess);
   if (!d_w || !d_w0 || !d_s || !d_ws || (rank > 0 && (!d_u || !d_v || !d_omega)))
     return report(WL_EINVAL, "NULL pointer", -1, hipSuccess);
   if (reinterpret_cast<uintptr_t>(d_ws) % 256) return report(WL_EINVAL, "workspace not 256-byte aligned", -1, hipSuccess);
-  if (ws_bytes < weightless_decompose_workspace_bytes(N, K, rank, oversample))
-    return report(WL_ENOSPACE, "workspace too small", -1, hipSuccess);
+  const size_t need = base_workspace_bytes(N, K, rank, oversample) + (sweeps > 0 ? als_extra_bytes(N, K) : 0);
+  if (ws_bytes < need) return report(WL_ENOSPACE, "workspace too small", -1, hipSuccess);
   const int l = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(rank) + oversample, std::min(N, K)));
   Dev d;
   d.s = static_cast<hipStream_t>(stream);
@@ -230,17 +237,16 @@ wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K,
   float *F = take(static_cast<size_t>(N) * rank), *F2 = take(static_cast<size_t>(K) * rank);
   d.part_elems = part_elems(N, K, l);
   d.part = take(d.part_elems);
+  float *num = sweeps > 0 ? take(static_cast<size_t>(N) * K) : nullptr;
+  float *den = sweeps > 0 ? take(static_cast<size_t>(N)) : nullptr;
 
   const uint16_t *W = static_cast<const uint16_t *>(d_w);
   uint16_t *W0 = static_cast<uint16_t *>(d_w0);
   uint16_t *Uo = static_cast<uint16_t *>(d_u), *Vo = static_cast<uint16_t *>(d_v);
   const size_t nk = static_cast<size_t>(N) * K;
-  d.err = wl::launch_band_mean(W, m, nk, W0, d.s);
-  if (!d.ok()) return report(WL_EHIP, "", -1, d.err);
-  for (int layer = 0; layer < m; ++layer) {
-    d.err = wl::launch_scale_residual(W + layer * nk, W0, N, K, d_s + static_cast<size_t>(layer) * N, R, d.s);
-    if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
-    if (rank == 0) continue;
+
+  // U V^T of R's layer (the residual R, already formed) -> the layer's bf16 U, V
+  auto svd_layer = [&](int layer) -> wl_status {
     uint16_t *u = Uo + static_cast<size_t>(layer) * N * rank, *v = Vo + static_cast<size_t>(layer) * K * rank;
     // range finder: Y = R Omega, then q rounds of Z = R^T Y, Y = R Z.  The
     // bases between products only need to stay well conditioned (one
@@ -256,12 +262,13 @@ wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K,
       o = d.ok() ? orthonormalize(d, Y, Y2, N, l, small, it + 1 == power_iters ? 3 : 1) : kOrthFail;
     }
     if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
-    if (o == kOrthFail) return report(WL_EINVAL, "range basis is not numerically positive definite (non-finite weights?)", layer, hipSuccess);
+    if (o == kOrthFail)
+      return report(WL_EINVAL, "range basis is not numerically positive definite (non-finite weights?)", layer,
+                    hipSuccess);
     if (o == kOrthZero) {  // R Omega = 0: the residual is zero, so is its delta
       d.err = hipMemsetAsync(u, 0, static_cast<size_t>(N) * rank * 2, d.s);
       if (d.ok()) d.err = hipMemsetAsync(v, 0, static_cast<size_t>(K) * rank * 2, d.s);
-      if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
-      continue;
+      return d.ok() ? WL_OK : report(WL_EHIP, "", layer, d.err);
     }
     // B = Q^T R [l, K]; B B^T = W Lambda W^T on the host
     d.err = d.gemm(Y, 1, l, R, K, 1, B, K, l, K, N);
@@ -286,12 +293,78 @@ wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K,
     d.put_async(Z2, d.up_v, Sv);
     if (d.ok()) d.err = d.gemm(B, 1, K, Z2, rank, 1, F2, rank, K, rank, l);
     if (d.ok()) d.err = wl::launch_to_bf16(F2, static_cast<size_t>(K) * rank, v, d.s);
+    return d.ok() ? WL_OK : report(WL_EHIP, "", layer, d.err);
+  };
+  // D = U V^T of a layer's stored (bf16) delta, fp32 into R; NULL for rank 0
+  auto delta_into_R = [&](int layer) -> const float * {
+    if (rank == 0) return nullptr;
+    const uint16_t *u = Uo + static_cast<size_t>(layer) * N * rank, *v = Vo + static_cast<size_t>(layer) * K * rank;
+    d.err = wl::launch_to_f32(u, static_cast<size_t>(N) * rank, F, d.s);
+    if (d.ok()) d.err = wl::launch_to_f32(v, static_cast<size_t>(K) * rank, F2, d.s);
+    if (d.ok()) d.err = d.gemm(F, rank, 1, F2, 1, rank, R, K, N, K, rank);
+    return R;
+  };
+
+  d.err = wl::launch_band_mean(W, m, nk, W0, d.s);
+  if (!d.ok()) return report(WL_EHIP, "", -1, d.err);
+  for (int layer = 0; layer < m; ++layer) {
+    d.err = wl::launch_scale_residual(W + layer * nk, W0, N, K, nullptr, d_s + static_cast<size_t>(layer) * N, R, d.s);
     if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
+    if (rank == 0) continue;
+    const wl_status st = svd_layer(layer);
+    if (st != WL_OK) return st;
+  }
+  for (int sweep = 0; sweep < sweeps; ++sweep) {
+    for (int layer = 0; layer < m; ++layer) {
+      const float *D = delta_into_R(layer);
+      if (d.ok())
+        d.err = wl::launch_w0_accumulate(W + layer * nk, D, d_s + static_cast<size_t>(layer) * N, N, K, num, den,
+                                         layer == 0, d.s);
+      if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
+    }
+    d.err = wl::launch_w0_finish(num, den, N, K, W0, d.s);
+    if (!d.ok()) return report(WL_EHIP, "", -1, d.err);
+    for (int layer = 0; layer < m; ++layer) {
+      const float *D = delta_into_R(layer);
+      if (d.ok())
+        d.err = wl::launch_scale_residual(W + layer * nk, W0, N, K, D, d_s + static_cast<size_t>(layer) * N, R, d.s);
+      if (!d.ok()) return report(WL_EHIP, "", layer, d.err);
+      if (rank == 0) continue;
+      const wl_status st = svd_layer(layer);
+      if (st != WL_OK) return st;
+    }
   }
   d.err = hipStreamSynchronize(d.s);
   if (!d.ok()) return report(WL_EHIP, "", m - 1, d.err);
   wl::set_last_error("");
   return WL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t weightless_decompose_workspace_bytes(int32_t N, int32_t K, int32_t rank, int32_t oversample) {
+  return base_workspace_bytes(N, K, rank, oversample);
+}
+
+wl_status weightless_decompose(const void *d_w, int32_t m, int32_t N, int32_t K, int32_t rank, int32_t oversample,
+                               int32_t power_iters, const float *d_omega, void *d_w0, float *d_s, void *d_u,
+                               void *d_v, void *d_ws, size_t ws_bytes, void *stream) {
+  return decompose_band(d_w, m, N, K, rank, oversample, power_iters, 0, d_omega, d_w0, d_s, d_u, d_v, d_ws, ws_bytes,
+                        stream);
+}
+
+size_t weightless_decompose_als_workspace_bytes(int32_t N, int32_t K, int32_t rank, int32_t oversample) {
+  const size_t base = base_workspace_bytes(N, K, rank, oversample);
+  return base ? base + als_extra_bytes(N, K) : 0;
+}
+
+wl_status weightless_decompose_als(const void *d_w, int32_t m, int32_t N, int32_t K, int32_t rank, int32_t oversample,
+                                   int32_t power_iters, int32_t sweeps, const float *d_omega, void *d_w0, float *d_s,
+                                   void *d_u, void *d_v, void *d_ws, size_t ws_bytes, void *stream) {
+  return decompose_band(d_w, m, N, K, rank, oversample, power_iters, sweeps, d_omega, d_w0, d_s, d_u, d_v, d_ws,
+                        ws_bytes, stream);
 }
 
 }  // extern "C"

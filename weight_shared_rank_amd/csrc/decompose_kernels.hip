@@ -4,7 +4,10 @@
 // are the analytic decomposition of the "Add a new model architecture" page
 // ("Decompose HF weights") with these readings: band mean, per-row scale
 // s_i = <W_i, W0_i> / <W0_i, W0_i>, rank-r truncated SVD of W - diag(s) W0
-// split as U = P sqrt(S), V = Q sqrt(S).
+// split as U = P sqrt(S), V = Q sqrt(S).  ALS sweeps ("Quality (Gemma 4 31B)"
+// page, "ALS optimization barely helps"; read as block-coordinate least
+// squares from that start) add the shared-block refit and a scale against
+// W0 with the layer's delta U V^T removed.
 #include <algorithm>
 
 #include "common.h"
@@ -27,15 +30,20 @@ __global__ void band_mean_kernel(const uint16_t *W, int m, size_t nk, uint16_t *
   W0[i] = f64_to_bf16(acc / m);
 }
 
-// s_i = <W_i, W0_i> / <W0_i, W0_i> in fp64 (1 for a zero W0 row), stored fp32;
-// then R_i = W_i - s_i W0_i in fp32.  One workgroup per row.
-__global__ void scale_residual_kernel(const uint16_t *W, const uint16_t *W0, int K, float *s, float *R) {
+// s_i = <W_i - D_i, W0_i> / <W0_i, W0_i> in fp64 (1 for a zero W0 row),
+// stored fp32, with D = U V^T of the layer's current delta (fp32 [N][K]; null
+// for none, the one-shot decomposition); then R_i = W_i - s_i W0_i in fp32.
+// One workgroup per row.  R may be D: a row's D is read in full before the
+// barrier and R written after it.
+__global__ void scale_residual_kernel(const uint16_t *W, const uint16_t *W0, int K, const float *D, float *s,
+                                      float *R) {
   const int row = blockIdx.x;
   const uint16_t *w = W + static_cast<size_t>(row) * K;
   const uint16_t *w0 = W0 + static_cast<size_t>(row) * K;
+  const float *d = D ? D + static_cast<size_t>(row) * K : nullptr;
   double num = 0.0, den = 0.0;
   for (int j = threadIdx.x; j < K; j += blockDim.x) {
-    const double a = bf16_to_f32(w[j]), b = bf16_to_f32(w0[j]);
+    const double a = bf16_to_f32(w[j]) - (d ? static_cast<double>(d[j]) : 0.0), b = bf16_to_f32(w0[j]);
     num += a * b;
     den += b * b;
   }
@@ -157,6 +165,35 @@ __global__ void reduce_kernel(const float *P, int splits, int M, int N, float *C
   C[(i / N) * ldc + i % N] = acc;
 }
 
+// ALS shared-block step, one layer: num_ij (+)= s_i (W_ij - D_ij), den_i (+)=
+// s_i^2 (fp32; layers are added in layer order, first == 1 starts the sums).
+// D null: no delta (rank 0).
+__global__ void w0_accumulate_kernel(const uint16_t *W, const float *D, const float *s, int N, int K, float *num,
+                                     float *den, int first) {
+  const size_t nk = static_cast<size_t>(N) * K;
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= nk) return;
+  const int row = static_cast<int>(i / K);
+  const float sv = s[row];
+  const float v = sv * (bf16_to_f32(W[i]) - (D ? D[i] : 0.f));
+  num[i] = first ? v : num[i] + v;
+  if (i % K == 0) den[row] = first ? sv * sv : den[row] + sv * sv;
+}
+
+// W0_ij = bf16(num_ij / den_i); a row whose scales were all zero keeps W0.
+__global__ void w0_finish_kernel(const float *num, const float *den, int K, size_t nk, uint16_t *W0) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= nk) return;
+  const float d = den[i / K];
+  if (d != 0.f) W0[i] = f32_to_bf16(num[i] / d);
+}
+
+// bf16 -> fp32, n elements.
+__global__ void to_f32_kernel(const uint16_t *src, size_t n, float *dst) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = bf16_to_f32(src[i]);
+}
+
 // fp32 -> bf16 (nearest even), n elements.
 __global__ void to_bf16_kernel(const float *src, size_t n, uint16_t *dst) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -172,9 +209,29 @@ hipError_t launch_band_mean(const uint16_t *W, int m, size_t nk, uint16_t *W0, h
   return hipGetLastError();
 }
 
-hipError_t launch_scale_residual(const uint16_t *W, const uint16_t *W0, int N, int K, float *s, float *R,
-                                 hipStream_t stream) {
-  hipLaunchKernelGGL(scale_residual_kernel, dim3(N), dim3(256), 0, stream, W, W0, K, s, R);
+hipError_t launch_scale_residual(const uint16_t *W, const uint16_t *W0, int N, int K, const float *D, float *s,
+                                 float *R, hipStream_t stream) {
+  hipLaunchKernelGGL(scale_residual_kernel, dim3(N), dim3(256), 0, stream, W, W0, K, D, s, R);
+  return hipGetLastError();
+}
+
+hipError_t launch_w0_accumulate(const uint16_t *W, const float *D, const float *s, int N, int K, float *num,
+                                float *den, bool first, hipStream_t stream) {
+  const size_t nk = static_cast<size_t>(N) * K;
+  hipLaunchKernelGGL(w0_accumulate_kernel, dim3(blocks_for(nk)), dim3(256), 0, stream, W, D, s, N, K, num, den,
+                     first ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_w0_finish(const float *num, const float *den, int N, int K, uint16_t *W0, hipStream_t stream) {
+  const size_t nk = static_cast<size_t>(N) * K;
+  hipLaunchKernelGGL(w0_finish_kernel, dim3(blocks_for(nk)), dim3(256), 0, stream, num, den, K, nk, W0);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f32(const uint16_t *src, size_t n, float *dst, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(to_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, src, n, dst);
   return hipGetLastError();
 }
 

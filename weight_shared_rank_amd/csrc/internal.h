@@ -92,13 +92,21 @@ hipError_t launch_dequantize_mxfp4(const uint8_t *codes, int32_t Kq, const uint8
                                    uint16_t *dst, hipStream_t stream);
 
 // Decomposition (one band of one family): W0 = bf16(mean of the m layers
-// W [m][nk]); per layer s [N] (LS row scale, fp32) and R = W - s W0 (fp32
-// [N][K]); a strided fp32 GEMM C = A B with A(m,k) = A[m*sam + k*sak] and
-// B(k,n) = B[k*sbk + n*sbn], splitting K over up to part_elems / (M N)
-// slices whose fp32 partials go to part (NULL: no split); fp32 -> bf16.
+// W [m][nk]); per layer s [N] (LS row scale of W - D against W0, fp32; D =
+// the layer's delta U V^T in fp32 [N][K], or NULL) and R = W - s W0 (fp32
+// [N][K]; may be D); a strided fp32 GEMM C = A B with A(m,k) = A[m*sam +
+// k*sak] and B(k,n) = B[k*sbk + n*sbn], splitting K over up to part_elems /
+// (M N) slices whose fp32 partials go to part (NULL: no split); fp32 -> bf16
+// and back.  ALS shared-block step: per layer num (+)= diag(s) (W - D), den
+// (+)= s^2 (first starts the sums), then W0 = bf16(num / den) on rows with
+// den != 0.
 hipError_t launch_band_mean(const uint16_t *W, int m, size_t nk, uint16_t *W0, hipStream_t stream);
-hipError_t launch_scale_residual(const uint16_t *W, const uint16_t *W0, int N, int K, float *s, float *R,
-                                 hipStream_t stream);
+hipError_t launch_scale_residual(const uint16_t *W, const uint16_t *W0, int N, int K, const float *D, float *s,
+                                 float *R, hipStream_t stream);
+hipError_t launch_w0_accumulate(const uint16_t *W, const float *D, const float *s, int N, int K, float *num,
+                                float *den, bool first, hipStream_t stream);
+hipError_t launch_w0_finish(const float *num, const float *den, int N, int K, uint16_t *W0, hipStream_t stream);
+hipError_t launch_to_f32(const uint16_t *src, size_t n, float *dst, hipStream_t stream);
 hipError_t launch_gemm_f32(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn,
                            float *C, int64_t ldc, int M, int N, int K, float *part, size_t part_elems,
                            hipStream_t stream);
