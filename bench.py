@@ -691,7 +691,9 @@ def decompose_section(dev, rank=32, over=16, q=4, cpu_budget=0.0, streams=16):
     the bands spread over `streams` host threads, each with its own stream
     and workspace (the calls are independent; a call's host factorizations
     then overlap the other calls' device work).  The model figure is the
-    concurrent one; the one-stream figure is reported beside it."""
+    concurrent one; the one-stream figure is reported beside it.  Then the
+    same model with one ALS sweep per band (weightless_decompose_als), and
+    the mean relative error of band 0's seven families with and without it."""
     import torch
     import synth
     from weight_shared_rank_amd import binding
@@ -709,17 +711,17 @@ def decompose_section(dev, rank=32, over=16, q=4, cpu_budget=0.0, streams=16):
     pool = ThreadPoolExecutor(streams)
     sts = [torch.cuda.Stream(device=dev) for _ in range(streams)]
 
-    def run(batch, nst):
+    def run(batch, nst, sweeps=None):
         if nst == 1:
             for w, om in batch:
-                binding.decompose(w, rank, om, oversample=over, power_iters=q)
+                binding.decompose(w, rank, om, oversample=over, power_iters=q, als_sweeps=sweeps)
             torch.cuda.synchronize()
             return
 
         def work(i):
             with torch.cuda.stream(sts[i]):
                 for w, om in batch[i::nst]:
-                    binding.decompose(w, rank, om, oversample=over, power_iters=q, stream=sts[i])
+                    binding.decompose(w, rank, om, oversample=over, power_iters=q, stream=sts[i], als_sweeps=sweeps)
             sts[i].synchronize()
         list(pool.map(work, range(nst)))
         torch.cuda.synchronize()
@@ -732,12 +734,28 @@ def decompose_section(dev, rank=32, over=16, q=4, cpu_budget=0.0, streams=16):
     t0 = time.perf_counter()
     run(inputs, streams)
     el = time.perf_counter() - t0
+    run(inputs[:2 * streams], streams, 1)   # warm-up of the ALS path
+    t0 = time.perf_counter()
+    run(inputs, streams, 1)
+    el_als = time.perf_counter() - t0
     pool.shutdown()
+    from oracle import decompose as odec
+
+    def band_error(sweeps):
+        errs = []
+        for w, om in inputs[:7]:
+            W0, sv, U, V = (t.float().cpu().double().numpy() for t in
+                            binding.decompose(w, rank, om, oversample=over, power_iters=q, als_sweeps=sweeps))
+            wl64 = w.float().cpu().double().numpy()
+            errs += [odec.rel_frobenius_error(wl64[i], W0, sv[i], U[i], V[i]) for i in range(2)]
+        return float(sum(errs) / len(errs))
     out = {"workload": "gemma3-1b decomposition: 13 bands x 7 families (q, k, v, o, gate, up, down), two layers "
                        "per band, rank 32, oversample 16, 4 power rounds",
            "matrices": 2 * len(inputs), "streams": streams, "seconds": el, "matrices_per_s": 2 * len(inputs) / el,
            "fp32_flops": flops, "fp32_TFLOPs": flops / el / 1e12,
-           "one_stream_seconds": el1, "one_stream_matrices_per_s": 2 * len(inputs) / el1}
+           "one_stream_seconds": el1, "one_stream_matrices_per_s": 2 * len(inputs) / el1,
+           "als_1_sweep": {"seconds": el_als, "matrices_per_s": 2 * len(inputs) / el_als,
+                           "band0_mean_error_one_shot": band_error(None), "band0_mean_error_als_1": band_error(1)}}
     if cpu_budget > 0:
         import numpy as np
         from oracle import decompose
@@ -955,6 +973,9 @@ def main():
             f"{res['decompose_gemma3']['seconds']:.2f} s for the gemma3 model on "
             f"{res['decompose_gemma3']['streams']} streams (one stream: "
             f"{res['decompose_gemma3']['one_stream_seconds']:.2f} s)")
+        als = res["decompose_gemma3"]["als_1_sweep"]
+        log(f"decomposition with one ALS sweep: {als['seconds']:.2f} s; band 0 mean error "
+            f"{als['band0_mean_error_one_shot']:.4f} -> {als['band0_mean_error_als_1']:.4f}")
 
     line = {"metric": "weightless-linear decode GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
