@@ -612,27 +612,39 @@ __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(1, 
     }
     __syncthreads();
     if (up_half) return;
+    // h = act(gate) * up into a token-major tile after the exchange area,
+    // then whole 16-byte chunks of H rows (as the fused y store)
+    constexpr int XCH = (WM / 2) * WN * TL::FM * TL::FN * 64 * static_cast<int>(sizeof(f32x4));
+    constexpr int HPITCH = 2 * HB + 16;  // bytes per token row (16-byte pad against bank conflicts)
+    static_assert(XCH + BN * HPITCH <= static_cast<int>(TL::LDS), "exchange and h tile fit the ring");
+    uint8_t *ht = lds + XCH;
 #pragma unroll
-    for (int j = 0; j < TL::FN; ++j) {
-      const int tok = n0 + wn * TL::TN + j * 16 + r16;
-      if (tok >= a.T) continue;
-      uint16_t *hrow = a.H + static_cast<int64_t>(tok) * a.ldh;
+    for (int j = 0; j < TL::FN; ++j)
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i) {
-        const int v = wm * TL::TM + i * 16 + g * 4;  // < BM/2: a gate row
-        const int nv = nvalid(v, 4), jj = actual(v);
         const f32x4 u = xch[((pw * TL::FM + i) * TL::FN + j) * 64 + lane];
         uint16_t o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(activation(a.act, acc[i][j][e]) * u[e]);
-        if (nv == 4 && (reinterpret_cast<uintptr_t>(hrow + jj) & 7) == 0) {
-          *reinterpret_cast<uint2 *>(hrow + jj) =
-              make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (e < nv) hrow[jj + e] = o[e];
-        }
+        // tile row: token; column: gate row v = wm TM + 16 i + 4 g (< BM/2)
+        *reinterpret_cast<uint2 *>(ht + (wn * TL::TN + j * 16 + r16) * HPITCH + (wm * TL::TM + i * 16 + g * 4) * 2) =
+            make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+      }
+    __syncthreads();  // the gate half's waves only: the up half has left
+    constexpr int CPR = HB / 8;                    // 16-byte chunks per token row
+    constexpr int NTHR = (WM / 2) * WN * 64;       // the gate half's threads, 0 .. NTHR-1
+    for (int c = threadIdx.x; c < BN * CPR; c += NTHR) {
+      const int tl = c / CPR, v = (c % CPR) * 8;
+      const int tok = n0 + tl;
+      const int nv = nvalid(v, 8), jj = actual(v);
+      if (tok >= a.T || nv == 0) continue;
+      const uint4 x = *reinterpret_cast<const uint4 *>(ht + tl * HPITCH + v * 2);
+      uint16_t *hrow = a.H + static_cast<int64_t>(tok) * a.ldh;
+      if (nv == 8 && (reinterpret_cast<uintptr_t>(hrow + jj) & 15) == 0) {
+        *reinterpret_cast<uint4 *>(hrow + jj) = x;
+      } else {
+        const uint16_t *o = reinterpret_cast<const uint16_t *>(&x);
+        for (int e = 0; e < nv; ++e) hrow[jj + e] = o[e];
       }
     }
     return;
