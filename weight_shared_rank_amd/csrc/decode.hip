@@ -113,6 +113,11 @@ constexpr int kFp4KsDiv = WL_FP4_KS_DIV;
 #define WL_VT_SPLIT_K 16384
 #endif
 constexpr int kVtSplitK = WL_VT_SPLIT_K;
+// from this K on, one-token bf16 calls give the V^T tiles longer k blocks
+#ifndef WL_VT_WIDE_K
+#define WL_VT_WIDE_K 5120
+#endif
+constexpr int kVtWideK = WL_VT_WIDE_K;
 
 // One batch of UNROLL complete k-steps (32 k each): loads first, then MFMAs.
 template <int UNROLL>
@@ -243,7 +248,9 @@ __device__ __forceinline__ void load_z8(const void *zbuf, int KSV, int T, int Rz
 // each split into KS slices of K.
 // XL (FP8 or MXFP4 W0 at T = 1): x staged in LDS (dynamic shared memory of
 // the slice's x row: ceil(pairs / KS) * 128 or ceil(quads / KS) * 256 bytes).
-template <int W, int UNROLL, bool XL = false>
+// VTU: k-steps per block for the V^T tiles (bf16 W0), which run the whole K
+// while a W0 workgroup runs one slice of it.
+template <int W, int UNROLL, bool XL = false, int VTU = UNROLL>
 __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_part, void *zbuf, int nwg_vt, int KSV,
                                                         int KS) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -378,9 +385,17 @@ __global__ __launch_bounds__(W * 64) void stream_kernel(CallDesc c, float *p_par
   } else {
     const uint16_t *arow = mat + static_cast<size_t>(arow_idx) * K + g * 8;
     const int nfull_end = min(s_end, K >> 5);  // steps entirely inside K
-    const int nblocks = max(0, nfull_end - s_begin) / UNROLL;
-    for (int b = wave; b < nblocks; b += W) kblock<UNROLL>(acc, arow, xrow, tok_ok, s_begin + b * UNROLL);
-    for (int s = s_begin + nblocks * UNROLL + wave; s < s_end; s += W) {
+    int s_tail;
+    if (VTU != UNROLL && vt) {
+      const int nblocks = max(0, nfull_end - s_begin) / VTU;
+      for (int b = wave; b < nblocks; b += W) kblock<VTU>(acc, arow, xrow, tok_ok, s_begin + b * VTU);
+      s_tail = s_begin + nblocks * VTU;
+    } else {
+      const int nblocks = max(0, nfull_end - s_begin) / UNROLL;
+      for (int b = wave; b < nblocks; b += W) kblock<UNROLL>(acc, arow, xrow, tok_ok, s_begin + b * UNROLL);
+      s_tail = s_begin + nblocks * UNROLL;
+    }
+    for (int s = s_tail + wave; s < s_end; s += W) {
       const bool kin = s * 32 + g * 8 < K;  // the last step may be partial
       const u32x4 a = kin ? ld16(arow + s * 32) : zero4;
       const u32x4 v = kin ? ld16(xrow + s * 32) : zero4;
@@ -820,6 +835,12 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
       }
       hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll, true>), dim3(nwg_vt + nt_w0 * KS),
                          dim3(kStreamWaves * 64), xbytes, stream, c, p_part, z_pair, nwg_vt, KSV, KS);
+    } else if (c.T == 1 && c.W0 != nullptr && c.K >= kVtWideK) {
+      // one token, long K: the V^T tiles (whole K) take blocks of twice the
+      // k-steps, so more of their bytes are in flight
+      hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll, false, 2 * kStreamUnroll>),
+                         dim3(nwg_vt + nt_w0 * KS), dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nwg_vt,
+                         KSV, KS);
     } else {
       hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll>), dim3(nwg_vt + nt_w0 * KS),
                          dim3(kStreamWaves * 64), 0, stream, c, p_part, z_pair, nwg_vt, KSV, KS);
