@@ -239,9 +239,9 @@ def test_split_k_prefill(gpu_lib, T):
 @pytest.mark.parametrize("rank", [5, 70])
 def test_long_k_decode_splits_vt(gpu_lib, rank):
     """At T = 1 with an FP8 shared block a K of 16384 or more splits the V^T
-    rows in two K slices whose fp32 partials the epilogue adds (bf16 keeps
-    them whole): ragged rows and ranks, single and stacked calls, both
-    formats, against the oracle."""
+    rows in two K slices whose fp32 partials the epilogue adds (with bf16,
+    calls of fewer than 4096 rows split them too): ragged rows and ranks,
+    single and stacked calls, both formats, against the oracle."""
     dims = {(0, "q"): (136, 16392), (0, "k"): (40, 16392), (0, "v"): (40, 16392), (0, "o"): (16392, 136),
             (0, "gate"): (72, 16384), (0, "up"): (72, 16384), (0, "down"): (16384, 72)}
     wl = synth.custom(2, 1, rank, dims, cid=79)
@@ -261,6 +261,32 @@ def test_long_k_decode_splits_vt(gpu_lib, rank):
             torch.cuda.synchronize()
             res = compare(np64(h), ow.gate_up_act(layer, np64(x), "gelu_tanh"))
             assert res["ok"], f"{fmt} layer {layer} gate_up_act: {res}"
+
+
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_small_call_decode_splits_vt(gpu_lib, T):
+    """bf16 decode calls of fewer than 4096 rows with K >= 2048 split their
+    V^T rows in two K slices (o here has 4104 rows and keeps them whole):
+    ragged rows, K and rank, single, stacked and fused-activation calls,
+    against the oracle."""
+    dims = {(0, "q"): (200, 4104), (0, "k"): (40, 4104), (0, "v"): (40, 4104), (0, "o"): (4104, 200),
+            (0, "gate"): (96, 2056), (0, "up"): (96, 2056), (0, "down"): (2056, 96)}
+    wl = synth.custom(2, 1, 37, dims, cid=83)
+    ow = OracleWorkload(wl, DEV)
+    b = sdev.load(wl, DEV)
+    for layer in range(2):
+        for c in ("qkv", "gate_up", "q", "o", "down"):
+            x = wl.x(layer, c, T, DEV)
+            announce(f"small-call decode T={T} layer {layer} {c}")
+            y = call(b, layer, c, x)
+            torch.cuda.synchronize()
+            res = compare(np64(y), ow.call(layer, c, np64(x)))
+            assert res["ok"], f"T={T} layer {layer} {c}: {res}"
+        x = wl.x(layer, "gate_up", T, DEV)
+        h = b.gate_up_act(layer, "silu", x)
+        torch.cuda.synchronize()
+        res = compare(np64(h), ow.gate_up_act(layer, np64(x), "silu"))
+        assert res["ok"], f"T={T} layer {layer} gate_up_act: {res}"
 
 
 @pytest.mark.parametrize("T", [40, 200])

@@ -118,6 +118,15 @@ constexpr int kVtSplitK = WL_VT_SPLIT_K;
 #define WL_VT_WIDE_K 5120
 #endif
 constexpr int kVtWideK = WL_VT_WIDE_K;
+// bf16 W0: calls with fewer rows than this and K >= WL_VT_SPLIT_MIN_K split
+// their V^T tiles in two K slices (their W0 stream is short, and a V^T tile
+// over the whole K would be the last workgroup still running)
+#ifndef WL_VT_SPLIT_ROWS
+#define WL_VT_SPLIT_ROWS 4096
+#endif
+#ifndef WL_VT_SPLIT_MIN_K
+#define WL_VT_SPLIT_MIN_K 2048
+#endif
 
 // One batch of UNROLL complete k-steps (32 k each): loads first, then MFMAs.
 template <int UNROLL>
@@ -820,8 +829,11 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
     // the whole K is the last workgroup still streaming: its rows are then
     // split in two K slices (FP8 down call 40.1 -> 33.7 us; with bf16 W0 the
     // split saved less in the stream launch than the epilogue's extra z
-    // loads cost)
+    // loads cost, except on calls with few rows: the Gemma-3 down call, 1152
+    // rows at K = 4096, ran its two 128 KB V^T tiles for most of its stream
+    // launch; split, the Gemma-3 step is 3% faster)
     KSV = ((c.W0f8 != nullptr || c.W0f4 != nullptr) && c.K >= kVtSplitK && KS >= 2) ? 2 : 1;
+    if (c.W0 != nullptr && c.Ntot < WL_VT_SPLIT_ROWS && c.K >= WL_VT_SPLIT_MIN_K && KS >= 2) KSV = 2;
     const int nwg_vt = (c.Rz + 15) / 16 * KSV;
     if (c.T == 1 && (c.W0f8 != nullptr || c.W0f4 != nullptr)) {
       // x slice in LDS: 64 k (128 bytes) per FP8 pair, 128 k per MXFP4 quad
