@@ -124,6 +124,15 @@ constexpr int kVtWideK = WL_VT_WIDE_K;
 #ifndef WL_VT_SPLIT_ROWS
 #define WL_VT_SPLIT_ROWS 4096
 #endif
+// bf16 W0, one-tile stream launch: slices shorter than this many k-steps
+// are merged when the split would need more than WL_RESIDENT_WGS workgroups
+// (about one round of resident 8-wave stream workgroups on the chip)
+#ifndef WL_SHORT_SLICE_STEPS
+#define WL_SHORT_SLICE_STEPS 32
+#endif
+#ifndef WL_RESIDENT_WGS
+#define WL_RESIDENT_WGS 768
+#endif
 #ifndef WL_VT_SPLIT_MIN_K
 #define WL_VT_SPLIT_MIN_K 2048
 #endif
@@ -824,6 +833,14 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
     KS = c.W0f8   ? max(1, decode_k_slices(c.Ntot, c.Rz, c.K) / WL_FP8_KS_DIV)
          : c.W0f4 ? max(1, (decode_k_slices(c.Ntot, c.Rz, c.K) + kFp4KsDiv - 1) / kFp4KsDiv)
                   : decode_k_slices(c.Ntot, c.Rz, c.K);
+    if (c.W0 != nullptr) {
+      // short slices: when the K split would take the launch past one round
+      // of resident workgroups, fewer slices (each wave then streams more
+      // of its rows) and a single round
+      const int tiles = (c.Ntot + 15) / 16 + (c.Rz + 15) / 16, nsteps = (c.K + 31) / 32;
+      if (nsteps / KS < WL_SHORT_SLICE_STEPS && tiles * KS > WL_RESIDENT_WGS && tiles <= WL_RESIDENT_WGS)
+        KS = max(1, WL_RESIDENT_WGS / tiles);
+    }
     // with a coded W0 (FP8, MXFP4) the W0 workgroups stream a half or a
     // quarter of the bytes, and over a long K (>= kVtSplitK) a V^T tile over
     // the whole K is the last workgroup still streaming: its rows are then
