@@ -113,6 +113,11 @@ constexpr int kFp4KsDiv = WL_FP4_KS_DIV;
 #define WL_VT_SPLIT_K 16384
 #endif
 constexpr int kVtSplitK = WL_VT_SPLIT_K;
+// and with an MXFP4 W0 (a quarter of the bytes) from this K on
+#ifndef WL_VT_SPLIT_K_FP4
+#define WL_VT_SPLIT_K_FP4 8192
+#endif
+constexpr int kVtSplitKFp4 = WL_VT_SPLIT_K_FP4;
 // from this K on, one-token bf16 calls give the V^T tiles longer k blocks
 #ifndef WL_VT_WIDE_K
 #define WL_VT_WIDE_K 5120
@@ -842,14 +847,17 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
         KS = max(1, WL_RESIDENT_WGS / tiles);
     }
     // with a coded W0 (FP8, MXFP4) the W0 workgroups stream a half or a
-    // quarter of the bytes, and over a long K (>= kVtSplitK) a V^T tile over
-    // the whole K is the last workgroup still streaming: its rows are then
-    // split in two K slices (FP8 down call 40.1 -> 33.7 us; with bf16 W0 the
+    // quarter of the bytes, and over a long K (>= kVtSplitK, or
+    // kVtSplitKFp4 for MXFP4) a V^T tile over the whole K is the last
+    // workgroup still streaming: its rows are then split in two K slices
+    // (FP8 down call 40.1 -> 33.7 us; MXFP4 o 22.0 -> 19.8 us, where the FP8
+    // o call was 1.4 us slower split; with bf16 W0 the
     // split saved less in the stream launch than the epilogue's extra z
     // loads cost, except on calls with few rows: the Gemma-3 down call, 1152
     // rows at K = 4096, ran its two 128 KB V^T tiles for most of its stream
     // launch; split, the Gemma-3 step is 3% faster)
-    KSV = ((c.W0f8 != nullptr || c.W0f4 != nullptr) && c.K >= kVtSplitK && KS >= 2) ? 2 : 1;
+    KSV = (((c.W0f8 != nullptr && c.K >= kVtSplitK) || (c.W0f4 != nullptr && c.K >= kVtSplitKFp4)) && KS >= 2)
+              ? 2 : 1;
     if (c.W0 != nullptr && c.Ntot < WL_VT_SPLIT_ROWS && c.K >= WL_VT_SPLIT_MIN_K && KS >= 2) KSV = 2;
     const int nwg_vt = (c.Rz + 15) / 16 * KSV;
     if (c.T == 1 && (c.W0f8 != nullptr || c.W0f4 != nullptr)) {
