@@ -289,6 +289,28 @@ def test_small_call_decode_splits_vt(gpu_lib, T):
         assert res["ok"], f"T={T} layer {layer} gate_up_act: {res}"
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_long_k_one_token_vt_blocks(gpu_lib, T):
+    """One-token bf16 calls with K >= 5120 stream their V^T tiles (the whole
+    K) in 8-step blocks; here K = 5130, so the last 32-k step is partial and
+    the block count leaves a tail of single steps, with 4100-row children
+    (no V^T split) and a ragged rank.  T = 2 takes the other kernels on the
+    same bundle."""
+    dims = {(0, "q"): (4100, 5128), (0, "k"): (1030, 5128), (0, "v"): (1030, 5128), (0, "o"): (5128, 4104),
+            (0, "gate"): (4104, 5128), (0, "up"): (4104, 5128), (0, "down"): (5128, 4104)}
+    wl = synth.custom(2, 1, 45, dims, cid=85)
+    ow = OracleWorkload(wl, DEV)
+    b = sdev.load(wl, DEV)
+    for layer in range(2):
+        for c in ("qkv", "gate_up", "q", "o", "down"):
+            x = wl.x(layer, c, T, DEV)
+            announce(f"long-K one-token V^T blocks T={T} layer {layer} {c}")
+            y = call(b, layer, c, x)
+            torch.cuda.synchronize()
+            res = compare(np64(y), ow.call(layer, c, np64(x)))
+            assert res["ok"], f"T={T} layer {layer} {c}: {res}"
+
+
 @pytest.mark.parametrize("T", [40, 200])
 def test_split_k_finish_with_unaligned_scale(gpu_lib, T):
     """A single-family call's s is a row slice of its group's s: after a q of
