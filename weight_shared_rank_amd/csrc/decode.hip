@@ -21,8 +21,11 @@
 //     for W0 rows.  V^T rows hold all of z = V^T x; they store it as a bf16
 //     pair, z_hi[t][rank] = bf16(z) and z_lo[t][rank] = bf16(z - z_hi), which
 //     keeps ~16 significant bits and is the MFMA operand of launch 2.
-//     The V^T tiles are not split (z needs no summation) and come first in
-//     the grid, so they are dispatched early and end well inside the launch.
+//     The V^T tiles come first in the grid, so they are dispatched early.
+//     They usually run the whole K (z then needs no summation).  Where a
+//     whole-K tile would be the launch's last workgroup, they are split in
+//     two K slices instead, and launch 2 adds the two fp32 halves of z.
+//     This covers coded W0 at long K and bf16 calls with few rows.
 //     With several tokens (bf16 W0) launch 1 is stream_rows_kernel instead:
 //     two or four 16-row tiles per workgroup share each x fragment, chosen
 //     by T and the call's slice lengths in launch_decode.
@@ -129,6 +132,9 @@ constexpr int kVtWideK = WL_VT_WIDE_K;
 #ifndef WL_VT_SPLIT_ROWS
 #define WL_VT_SPLIT_ROWS 4096
 #endif
+#ifndef WL_VT_SPLIT_MIN_K
+#define WL_VT_SPLIT_MIN_K 2048
+#endif
 // bf16 W0, one-tile stream launch: slices shorter than this many k-steps
 // are merged when the split would need more than WL_RESIDENT_WGS workgroups
 // (about one round of resident 8-wave stream workgroups on the chip)
@@ -137,9 +143,6 @@ constexpr int kVtWideK = WL_VT_WIDE_K;
 #endif
 #ifndef WL_RESIDENT_WGS
 #define WL_RESIDENT_WGS 768
-#endif
-#ifndef WL_VT_SPLIT_MIN_K
-#define WL_VT_SPLIT_MIN_K 2048
 #endif
 
 // One batch of UNROLL complete k-steps (32 k each): loads first, then MFMAs.
@@ -851,11 +854,10 @@ hipError_t launch_decode(const CallDesc &c, float *p_part, void *z_pair, hipStre
     // kVtSplitKFp4 for MXFP4) a V^T tile over the whole K is the last
     // workgroup still streaming: its rows are then split in two K slices
     // (FP8 down call 40.1 -> 33.7 us; MXFP4 o 22.0 -> 19.8 us, where the FP8
-    // o call was 1.4 us slower split; with bf16 W0 the
-    // split saved less in the stream launch than the epilogue's extra z
-    // loads cost, except on calls with few rows: the Gemma-3 down call, 1152
-    // rows at K = 4096, ran its two 128 KB V^T tiles for most of its stream
-    // launch; split, the Gemma-3 step is 3% faster)
+    // o call was 1.4 us slower split).  With bf16 W0 the split saves less in
+    // the stream launch than the epilogue's extra z loads cost, except on
+    // calls with few rows: the Gemma-3 down call, 1152 rows at K = 4096,
+    // ran its two 128 KB V^T tiles for most of its stream launch.
     KSV = (((c.W0f8 != nullptr && c.K >= kVtSplitK) || (c.W0f4 != nullptr && c.K >= kVtSplitKFp4)) && KS >= 2)
               ? 2 : 1;
     if (c.W0 != nullptr && c.Ntot < WL_VT_SPLIT_ROWS && c.K >= WL_VT_SPLIT_MIN_K && KS >= 2) KSV = 2;
